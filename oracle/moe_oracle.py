@@ -1,0 +1,312 @@
+"""CPU oracle for the dynamic any-precision MoE FFN layer (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library or its
+Python binding and imports nothing from them.
+
+Each function states the plain definition it computes and the passage of the
+pages it follows.  Pages, by title:
+  [DPA]  "DPA-MoE: A Runtime Precision Control Framework for MoE Inference"
+         (abstract; news summary "DPA-MoE enables dynamic precision routing
+         for expert selection").
+  [DUO]  "DuoRate: Two-Rate Per-Expert Precision Allocation for
+         Mixture-of-Experts Serving" (abstract).
+  [MAT]  "MatMoE: Matryoshka Mixture-of-Experts with Dynamic Mixed-Precision
+         Quantization for Efficient Inference" (abstract and the review's
+         sections Core Contribution, Methodological Rigor, Strengths,
+         Limitations).
+
+Readings taken where the pages are silent are listed next to the function
+that takes them.  Parity status: every function here is pinned by tests
+under tests/ (closed forms, brute force, library special cases); none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# stored checkpoint -> integer codes
+
+
+def plane_word_and_bit(n, c, N: int, K: int):
+    """Position of the bit of (row n, column c) inside one plane of an N x K
+    matrix: (word index within the plane, bit index within the word).
+
+    Layout (the stored format; [MAT] Core Contribution, bitplane storage):
+    rows in tiles of 16, columns in 128-column blocks of four 32-column
+    chunks; the words of one (row, chunk) for up to four consecutive blocks
+    are adjacent.  Works elementwise on NumPy integer arrays."""
+    nkb = K // 128
+    tile = n // 16
+    r = n % 16
+    kb = c // 128
+    j = (c % 128) // 32
+    bit = c % 32
+    quad = kb // 4
+    nq = np.minimum(4, nkb - 4 * quad)
+    lane = 16 * j + r
+    word = tile * (16 * K // 32) + 256 * quad + lane * nq + (kb % 4)
+    return word, bit
+
+
+def unpack_codes(planes: np.ndarray, b_max: int, N: int, K: int) -> np.ndarray:
+    """Unsigned codes q[e, n, c] = sum_p bit_p * 2^(b_max-1-p), plane 0 being
+    the most significant bit ([MAT] Core Contribution: bitplane storage;
+    [DPA] prefix-decodable chunks).  planes: uint32 [E, b_max, words]."""
+    planes = np.asarray(planes)
+    E = planes.shape[0]
+    n = np.arange(N)[:, None]
+    c = np.arange(K)[None, :]
+    word, bit = plane_word_and_bit(n, c, N, K)
+    q = np.zeros((E, N, K), dtype=np.int64)
+    for p in range(b_max):
+        w = planes[:, p, :].astype(np.int64)[:, word]          # [E, N, K]
+        q += ((w >> bit) & 1) << (b_max - 1 - p)
+    return q
+
+
+def unpack_scale_zero(sz: np.ndarray, N: int, G: int):
+    """sz float32 [E, N/16, G, 16, 2] -> (scale, zero) float64 [E, N, G]."""
+    sz = np.asarray(sz, dtype=np.float64)
+    E = sz.shape[0]
+    a = sz.transpose(0, 1, 3, 2, 4).reshape(E, N, G, 2)
+    return a[..., 0].copy(), a[..., 1].copy()
+
+
+# ---------------------------------------------------------------------------
+# floor-and-compensation dequantisation
+
+
+def fc_constant(delta: int) -> float:
+    """Compensation added after dropping `delta` low bits: (2^delta - 1)/2, the
+    mean of a residual uniform on {0, ..., 2^delta - 1} ([MAT] Core
+    Contribution, floor-and-compensation paragraph; the constant is printed
+    there without its opening parenthesis)."""
+    return (2.0 ** delta - 1.0) / 2.0
+
+
+def fc_codes(q: np.ndarray, b: int, b_max: int) -> np.ndarray:
+    """Code read from the first b planes with F&C: keep the top b bits of q
+    (floor of q / 2^delta), put them back in place and add the compensation
+    ([MAT] abstract item (2) and Core Contribution, F&C paragraph)."""
+    delta = b_max - b
+    qb = np.asarray(q, dtype=np.int64) >> delta
+    return (qb << delta).astype(np.float64) + fc_constant(delta)
+
+
+def floor_codes(q: np.ndarray, b: int, b_max: int) -> np.ndarray:
+    """Negative control: truncation without compensation (the plain floor that
+    the MatMoE review, Methodological Rigor, reports as collapsing)."""
+    delta = b_max - b
+    return ((np.asarray(q, dtype=np.int64) >> delta) << delta).astype(np.float64)
+
+
+def dequant(q: np.ndarray, scale: np.ndarray, zero: np.ndarray, b: int, b_max: int,
+            g: int, compensate: bool = True) -> np.ndarray:
+    """w_hat = (code_b - z) * s, with (s, z) of group floor(c/g) of the row,
+    shared by every read width ([DPA] SharedScale; [MAT] Core Contribution,
+    shared quantisation parameters).  q [.., N, K]; scale, zero [.., N, K/g].
+    Exact in float64 (code_b - z is a multiple of 1/2 below 16 in size)."""
+    codes = fc_codes(q, b, b_max) if compensate else floor_codes(q, b, b_max)
+    s = np.repeat(np.asarray(scale, dtype=np.float64), g, axis=-1)
+    z = np.repeat(np.asarray(zero, dtype=np.float64), g, axis=-1)
+    return (codes - z) * s
+
+
+# ---------------------------------------------------------------------------
+# router
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def router_logits(x_bf16: np.ndarray, w_router: np.ndarray, logit_bias=None) -> np.ndarray:
+    """l[t, e] = sum_i W_r[e, i] x[t, i] (+ bias_e), float64 ([DPA] abstract:
+    routing each token to a small set of experts; [MAT] routing scores)."""
+    x = bf16_to_f64(x_bf16)
+    l = x @ np.asarray(w_router, dtype=np.float64).T
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """p = exp(l - max) / sum exp(l - max) along the expert axis."""
+    m = l.max(axis=-1, keepdims=True)
+    e = np.exp(l - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def topk(l: np.ndarray, k: int):
+    """Top-k experts per token ordered by (logit descending, index ascending).
+    Returns idx [T, k] and the gap l_(k) - l_(k+1) per token (inf if k == E),
+    used to flag near-ties."""
+    T, E = l.shape
+    idx = np.empty((T, k), dtype=np.int64)
+    gap = np.full(T, np.inf)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-l[t, e], e))
+        idx[t] = order[:k]
+        if k < E:
+            gap[t] = l[t, order[k - 1]] - l[t, order[k]]
+    return idx, gap
+
+
+def route(x_bf16, w_router, logit_bias, k: int, renorm: bool = False):
+    """Gate scores of the chosen experts: softmax over all experts, then the
+    top k; renormalised over the k only if asked (reading: the pages say
+    "gate scores"/"routing score" without fixing renormalisation)."""
+    l = router_logits(x_bf16, w_router, logit_bias)
+    p = softmax(l)
+    idx, gap = topk(l, k)
+    gate = np.take_along_axis(p, idx, axis=1)
+    if renorm:
+        gate = gate / gate.sum(axis=1, keepdims=True)
+    return idx, gate, gap, l
+
+
+# ---------------------------------------------------------------------------
+# bit allocation
+
+
+def n_star(P: int, b_lo: int, b_max: int, target) -> int:
+    """Budget in high-precision pairs: floor(P (b* - B_lo) / (B_max - B_lo)),
+    exact rational arithmetic on the float32 value of b*, clamped to [0, P]
+    (reading: the budget is never exceeded)."""
+    t = Fraction(float(np.float32(target)))
+    if b_max == b_lo:
+        return 0
+    v = Fraction(P) * (t - b_lo) / (b_max - b_lo)
+    return max(0, min(P, math.floor(v)))
+
+
+def allocate_bits(gates: np.ndarray, b_lo: int, b_max: int, target):
+    """Threshold allocation over the live routed pairs of the batch ([MAT]
+    abstract item (3); Core Contribution: pairs whose routing score exceeds a
+    threshold run at high precision, the rest low, the threshold set to hit a
+    target average bit-width; [DPA] post-routing allocation from live gate
+    scores).
+
+    Plain definition by sorting: with scores sorted s_(1) >= ... >= s_(P),
+    start from n = n*, and while 0 < n < P and s_(n) == s_(n+1) step n down
+    (a threshold can not split equal scores).  The n highest pairs read B_max,
+    the rest B_lo.  Returns (bits [P] int, n, n*)."""
+    g = np.asarray(gates, dtype=np.float64).ravel()
+    P = g.size
+    ns = n_star(P, b_lo, b_max, target)
+    s = np.sort(g)[::-1]
+    n = ns
+    while 0 < n < P and s[n - 1] == s[n]:
+        n -= 1
+    bits = np.full(P, b_lo, dtype=np.int64)
+    if n == P:
+        bits[:] = b_max
+    elif n > 0:
+        bits[g > s[n]] = b_max
+    return bits, n, ns
+
+
+def threshold_interval(gates: np.ndarray, n: int):
+    """The thresholds tau with #{g > tau} == n form [s_(n+1), s_(n)); returns
+    that half-open interval (None for an open end)."""
+    s = np.sort(np.asarray(gates, dtype=np.float64).ravel())[::-1]
+    P = s.size
+    lo = s[n] if n < P else None
+    hi = s[n - 1] if n > 0 else None
+    return lo, hi
+
+
+# ---------------------------------------------------------------------------
+# expert FFN
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits),
+    ties to even."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.round(m * 256.0), e - 8)
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def expert_ffn(x: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """SwiGLU expert: g = W_gate x, u = W_up x, h = silu(g) u rounded to
+    bfloat16 (reading: activations between the projections are bf16, as the
+    layer's inputs are), o = W_down h.  w13 [2f, d] (gate rows first), w2 [d, f]."""
+    f = w13.shape[0] // 2
+    gu = w13 @ x
+    h = round_bf16(silu(gu[:f]) * gu[f:])
+    return w2 @ h
+
+
+class DequantCache:
+    """Dequantised matrices of one bank, computed on demand per (expert, bits)."""
+
+    def __init__(self, planes13, sz13, planes2, sz2, d: int, f: int, g: int, b_max: int):
+        self.p13, self.sz13, self.p2, self.sz2 = planes13, sz13, planes2, sz2
+        self.d, self.f, self.g, self.b_max = d, f, g, b_max
+        self._q = {}
+        self._w = {}
+
+    def codes(self, e: int):
+        if e not in self._q:
+            d, f, g, B = self.d, self.f, self.g, self.b_max
+            q13 = unpack_codes(self.p13[e:e + 1], B, 2 * f, d)[0]
+            q2 = unpack_codes(self.p2[e:e + 1], B, d, f)[0]
+            s13, z13 = unpack_scale_zero(self.sz13[e:e + 1], 2 * f, d // g)
+            s2, z2 = unpack_scale_zero(self.sz2[e:e + 1], d, f // g)
+            self._q[e] = (q13, s13[0], z13[0], q2, s2[0], z2[0])
+        return self._q[e]
+
+    def weights(self, e: int, b: int):
+        key = (e, b)
+        if key not in self._w:
+            q13, s13, z13, q2, s2, z2 = self.codes(e)
+            self._w[key] = (dequant(q13, s13, z13, b, self.b_max, self.g),
+                            dequant(q2, s2, z2, b, self.b_max, self.g))
+        return self._w[key]
+
+
+def bank_cache(bank) -> DequantCache:
+    return DequantCache(bank.w13_planes, bank.w13_sz, bank.w2_planes, bank.w2_sz,
+                        bank.d, bank.f, bank.g, bank.b_max)
+
+
+def combine(x_bf16, idx, gate, bits, routed: DequantCache, shared: DequantCache = None,
+            n_shared: int = 0, tokens=None) -> np.ndarray:
+    """y[t] = sum_j gate[t, j] * FFN_{idx[t, j]}^(bits[t, j])(x_t)
+    + sum_s FFN_shared_s^(b_max)(x_t); float64.  `tokens` restricts the
+    rows computed (others stay zero)."""
+    x = bf16_to_f64(x_bf16)
+    T, k = idx.shape
+    d = x.shape[1]
+    bits = np.asarray(bits).reshape(T, k)
+    y = np.zeros((T, d))
+    rows = range(T) if tokens is None else tokens
+    for t in rows:
+        for j in range(k):
+            w13, w2 = routed.weights(int(idx[t, j]), int(bits[t, j]))
+            y[t] += gate[t, j] * expert_ffn(x[t], w13, w2)
+        for s in range(n_shared):
+            w13, w2 = shared.weights(s, shared.b_max)
+            y[t] += expert_ffn(x[t], w13, w2)
+    return y
+
+
+def layer(x_bf16, w_router, logit_bias, k: int, b_lo: int, b_max: int, target,
+          routed: DequantCache, shared: DequantCache = None, n_shared: int = 0,
+          renorm: bool = False, tokens=None) -> dict:
+    """One full layer step: route, allocate, per-pair FFN, combine."""
+    idx, gate, gap, logits = route(x_bf16, w_router, logit_bias, k, renorm)
+    bits, n, ns = allocate_bits(gate, b_lo, b_max, target)
+    y = combine(x_bf16, idx, gate, bits, routed, shared, n_shared, tokens)
+    return dict(idx=idx, gate=gate, gap=gap, logits=logits, bits=bits, n_hi=n, n_star=ns, y=y)
