@@ -1,0 +1,266 @@
+"""ctypes binding of libmoe_anyprec.so (argument marshalling only).
+
+Every function mirrors one C entry point of include/moe_anyprec.h: it checks
+that the torch tensors it is given live on the GPU with the expected dtype and
+contiguity, passes their device pointers and the current HIP stream, and
+raises MoeError on a non-zero status.  No step of the layer is computed here;
+there is no fallback when the library is missing."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_anyprec.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe_anyprec.h")
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_RANGE",
+          5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_UNSUPPORTED", 7: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+
+
+class ExpertBankC(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("b_max", ctypes.c_int32),
+                ("w13_planes", ctypes.c_void_p), ("w13_sz", ctypes.c_void_p),
+                ("w2_planes", ctypes.c_void_p), ("w2_sz", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dynamic_any_precision_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        bp = ctypes.POINTER(ExpertBankC)
+        sig = {
+            "moe_route_workspace_bytes": (sz, [i32, i32]),
+            "moe_route": (i32, [vp, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
+            "moe_alloc_bits": (i32, [vp, i32, i32, i32, f32, vp, vp, vp, vp]),
+            "moe_budget_pairs": (i32, [i32, i32, i32, f32]),
+            "moe_ffn_workspace_bytes": (sz, [bp, bp, i32, i32]),
+            "moe_anyprec_ffn": (i32, [bp, bp, vp, i32, i32, vp, vp, vp, vp, i32, vp, sz, vp]),
+            "moe_permute": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
+            "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
+            "moe_status_string": (ctypes.c_char_p, [i32]),
+            "moe_last_hip_error": (i32, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/moe_anyprec.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = lib().moe_status_string(status).decode()
+        if status == 7:
+            detail += f", hipError={lib().moe_last_hip_error()}"
+        raise MoeError(status, where, detail)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+# ---------------------------------------------------------------------------
+# expert banks on the device
+
+
+@dataclass
+class DeviceBank:
+    n_experts: int
+    d: int
+    f: int
+    g: int
+    b_max: int
+    w13_planes: torch.Tensor
+    w13_sz: torch.Tensor
+    w2_planes: torch.Tensor
+    w2_sz: torch.Tensor
+
+    @classmethod
+    def from_host(cls, bank, device="cuda") -> "DeviceBank":
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint32:
+                a = a.view(np.int32)
+            return torch.from_numpy(a).to(device)
+        return cls(bank.n_experts, bank.d, bank.f, bank.g, bank.b_max,
+                   up(bank.w13_planes), up(bank.w13_sz), up(bank.w2_planes), up(bank.w2_sz))
+
+    def clone(self) -> "DeviceBank":
+        return DeviceBank(self.n_experts, self.d, self.f, self.g, self.b_max, self.w13_planes.clone(),
+                          self.w13_sz.clone(), self.w2_planes.clone(), self.w2_sz.clone())
+
+    def struct(self) -> ExpertBankC:
+        for t in (self.w13_planes, self.w13_sz, self.w2_planes, self.w2_sz):
+            _ptr(t, name="bank")
+        return ExpertBankC(self.n_experts, self.d, self.f, self.g, self.b_max,
+                           self.w13_planes.data_ptr(), self.w13_sz.data_ptr(),
+                           self.w2_planes.data_ptr(), self.w2_sz.data_ptr())
+
+    def plane_bytes_per_expert(self, bits: int) -> int:
+        """Bytes of the first `bits` planes of W13 and W2 of one expert."""
+        return bits * 3 * self.d * self.f // 8
+
+    def sz_bytes_per_expert(self) -> int:
+        return 3 * self.d * self.f // self.g * 8
+
+
+def _bank_struct(b: Optional[DeviceBank]):
+    return None if b is None else ctypes.byref(b.struct())
+
+
+# ---------------------------------------------------------------------------
+# entry points
+
+
+def route_workspace_bytes(T: int, E: int) -> int:
+    return int(lib().moe_route_workspace_bytes(T, E))
+
+
+def route_workspace(T: int, E: int, device="cuda") -> torch.Tensor:
+    """Zero-filled router workspace (its counters must start at zero)."""
+    n = route_workspace_bytes(T, E)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def route(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor], top_k: int,
+          renorm: bool = False, workspace: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+          gate: Optional[torch.Tensor] = None, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    if workspace is None:
+        workspace = route_workspace(T, E, x.device)
+    if idx is None:
+        idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+    if gate is None:
+        gate = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+    st = lib().moe_route(_ptr(x, _BF16, "x"), T, d, _ptr(w_router, torch.float32, "w_router"), E,
+                         _ptr(logit_bias, torch.float32, "logit_bias"), top_k, int(renorm),
+                         _ptr(idx, torch.int32, "topk_idx"), _ptr(gate, torch.float32, "topk_gate"),
+                         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                         _stream(stream))
+    _check(st, "moe_route")
+    return idx, gate
+
+
+def budget_pairs(P: int, b_lo: int, b_max: int, target: float) -> int:
+    return int(lib().moe_budget_pairs(P, b_lo, b_max, float(target)))
+
+
+def alloc_bits(gate: torch.Tensor, b_lo: int, b_max: int, target: float, bits: Optional[torch.Tensor] = None,
+               tau: Optional[torch.Tensor] = None, n_hi: Optional[torch.Tensor] = None, stream=None):
+    P = gate.numel()
+    if bits is None:
+        bits = torch.empty(P, dtype=torch.uint8, device=gate.device)
+    st = lib().moe_alloc_bits(_ptr(gate, torch.float32, "gate"), P, b_lo, b_max, float(target),
+                              _ptr(bits, torch.uint8, "bits"), _ptr(tau, torch.float32, "tau"),
+                              _ptr(n_hi, torch.int32, "n_hi"), _stream(stream))
+    _check(st, "moe_alloc_bits")
+    return bits
+
+
+def ffn_workspace_bytes(routed: DeviceBank, shared: Optional[DeviceBank], T: int, top_k: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(ctypes.byref(routed.struct()), _bank_struct(shared), T, top_k))
+
+
+def ffn_workspace(routed: DeviceBank, shared: Optional[DeviceBank], T: int, top_k: int, device="cuda"):
+    n = ffn_workspace_bytes(routed, shared, T, top_k)
+    if n == 0 and T > 0:
+        raise MoeError(2, "moe_ffn_workspace_bytes", "invalid bank or sizes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def anyprec_ffn(routed: DeviceBank, shared: Optional[DeviceBank], x: torch.Tensor, idx: torch.Tensor,
+                gate: torch.Tensor, bits: torch.Tensor, y: Optional[torch.Tensor] = None, accumulate: bool = False,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, d = x.shape
+    k = idx.shape[1]
+    if workspace is None:
+        workspace = ffn_workspace(routed, shared, T, k, x.device)
+    if y is None:
+        y = torch.zeros(T, d, dtype=torch.float32, device=x.device)
+    st = lib().moe_anyprec_ffn(ctypes.byref(routed.struct()), _bank_struct(shared), _ptr(x, _BF16, "x"), T, k,
+                               _ptr(idx, torch.int32, "topk_idx"), _ptr(gate, torch.float32, "topk_gate"),
+                               _ptr(bits, torch.uint8, "bits"), _ptr(y, torch.float32, "y"), int(accumulate),
+                               _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(st, "moe_anyprec_ffn")
+    return y
+
+
+def permute(idx: torch.Tensor, bits: torch.Tensor, E: int, b_max: int, workspace: torch.Tensor, stream=None):
+    T, k = idx.shape
+    slot_pair = torch.empty(T * k, dtype=torch.int32, device=idx.device)
+    eoff = torch.empty(E + 1, dtype=torch.int32, device=idx.device)
+    emax = torch.empty(E, dtype=torch.int32, device=idx.device)
+    st = lib().moe_permute(_ptr(idx, torch.int32, "topk_idx"), _ptr(bits, torch.uint8, "bits"), T, k, E, b_max,
+                           slot_pair.data_ptr(), eoff.data_ptr(), emax.data_ptr(), _ptr(workspace, name="workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_permute")
+    return slot_pair, eoff, emax
+
+
+def dequant(bank: DeviceBank, expert: int, matrix: int, bits: int, stream=None) -> torch.Tensor:
+    shape = (2 * bank.f, bank.d) if matrix == 0 else (bank.d, bank.f)
+    out = torch.empty(shape, dtype=torch.float32, device=bank.w13_planes.device)
+    st = lib().moe_dequant(ctypes.byref(bank.struct()), expert, matrix, bits, out.data_ptr(), _stream(stream))
+    _check(st, "moe_dequant")
+    return out
+
+
+def residual_to_bf16(h: torch.Tensor, x: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if x is None:
+        x = torch.empty(h.shape, dtype=torch.bfloat16, device=h.device)
+    st = lib().moe_residual_to_bf16(_ptr(h, torch.float32, "h"), _ptr(x, _BF16, "x"), h.numel(), _stream(stream))
+    _check(st, "moe_residual_to_bf16")
+    return x
+
+
+def bf16_tensor(bits_u16: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload bf16 bit patterns (numpy uint16) as a torch bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(device).view(torch.bfloat16)

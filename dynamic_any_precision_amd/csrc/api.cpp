@@ -1,0 +1,237 @@
+// C ABI of libmoe_anyprec: argument validation, workspace plans and launches.
+// Validation runs on the host before any HIP call, so it works without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe_anyprec.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int num_cu_cached() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+moe_status check_bank(const moe_expert_bank* b, bool need_ptrs) {
+  if (!b) return MOE_ERR_NULL;
+  if (need_ptrs && (!b->w13_planes || !b->w13_sz || !b->w2_planes || !b->w2_sz)) return MOE_ERR_NULL;
+  if (b->n_experts < 1 || b->b_max < 1 || b->b_max > 4) return MOE_ERR_RANGE;
+  if (b->group != 64 && b->group != 128) return MOE_ERR_UNSUPPORTED;
+  if (b->d_model < 128 || b->d_ff < 128 || b->d_model % 128 || b->d_ff % 128) return MOE_ERR_SHAPE;
+  if (need_ptrs && (!aligned(b->w13_planes, 16) || !aligned(b->w2_planes, 16) || !aligned(b->w13_sz, 16) ||
+                    !aligned(b->w2_sz, 16)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// floor(P * (target - b_lo) / (b_max - b_lo)) with exact arithmetic on the
+// float value of target (a dyadic rational), clamped to [0, P].
+int32_t exact_budget(int32_t P, int32_t b_lo, int32_t b_max, float target) {
+  if (P <= 0 || b_max <= b_lo) return 0;
+  int e = 0;
+  const double fr = std::frexp((double)target, &e);
+  const int64_t m = (int64_t)std::ldexp(fr, 24);
+  const int ex = e - 24;
+  __int128 num, den;
+  if (ex >= 0) {
+    num = (__int128)P * (((__int128)m << ex) - b_lo);
+    den = (__int128)(b_max - b_lo);
+  } else {
+    num = (__int128)P * ((__int128)m - ((__int128)b_lo << (-ex)));
+    den = (__int128)(b_max - b_lo) << (-ex);
+  }
+  __int128 q = num / den;
+  if ((num % den != 0) && ((num < 0) != (den < 0))) q -= 1;
+  if (q < 0) q = 0;
+  if (q > P) q = P;
+  return (int32_t)q;
+}
+
+moe::MatrixDev w13_of(const moe_expert_bank* b) {
+  moe::MatrixDev m;
+  m.planes = b->w13_planes;
+  m.sz = b->w13_sz;
+  m.N = 2 * b->d_ff;
+  m.K = b->d_model;
+  return m;
+}
+
+moe::MatrixDev w2_of(const moe_expert_bank* b) {
+  moe::MatrixDev m;
+  m.planes = b->w2_planes;
+  m.sz = b->w2_sz;
+  m.N = b->d_model;
+  m.K = b->d_ff;
+  return m;
+}
+
+moe_status ffn_shape(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T, int32_t top_k,
+                     bool need_ptrs, moe::FfnShape* out) {
+  moe_status st = check_bank(routed, need_ptrs);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    st = check_bank(shared, need_ptrs);
+    if (st != MOE_OK) return st;
+    if (shared->d_model != routed->d_model || shared->group != routed->group || shared->b_max != routed->b_max)
+      return MOE_ERR_SHAPE;
+    if (shared->n_experts > 16) return MOE_ERR_RANGE;
+  }
+  if (T < 0 || top_k < 1 || top_k > 8 || top_k > routed->n_experts || routed->n_experts > 256) return MOE_ERR_RANGE;
+  if ((int64_t)T * top_k + (shared ? (int64_t)shared->n_experts * T : 0) >= (1 << 24)) return MOE_ERR_RANGE;
+  *out = moe::make_shape(T, top_k, routed->n_experts, routed->b_max, routed->group, routed->d_model, routed->d_ff,
+                         shared ? shared->n_experts : 0, shared ? shared->d_ff : 0);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL";
+    case MOE_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case MOE_ERR_ALIGN: return "buffer not aligned";
+    case MOE_ERR_RANGE: return "argument out of range";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return moe::route_workspace_bytes(T, E);
+}
+
+moe_status moe_route(const uint16_t* x, int32_t T, int32_t d, const float* w_router, int32_t E,
+                     const float* logit_bias, int32_t top_k, int32_t renorm_topk, int32_t* topk_idx,
+                     float* topk_gate, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || top_k < 1 || top_k > 8 || top_k > E) return MOE_ERR_RANGE;
+  if (d < 128 || d % 128) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(workspace, 16)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe::route_workspace_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(x, T, d, w_router, E, logit_bias, top_k, renorm_topk, topk_idx, topk_gate,
+                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_budget_pairs(int32_t P, int32_t b_lo, int32_t b_max, float target_avg_bits) {
+  return exact_budget(P, b_lo, b_max, target_avg_bits);
+}
+
+moe_status moe_alloc_bits(const float* gate, int32_t P, int32_t b_lo, int32_t b_max, float target_avg_bits,
+                          uint8_t* bits, float* tau_out, int32_t* n_hi_out, void* stream) {
+  if (P < 0 || b_lo < 1 || b_max > 4 || b_lo > b_max) return MOE_ERR_RANGE;
+  if (!(target_avg_bits >= (float)b_lo && target_avg_bits <= (float)b_max)) return MOE_ERR_RANGE;
+  if (P == 0) return MOE_OK;
+  if (!gate || !bits) return MOE_ERR_NULL;
+  const int32_t ns = exact_budget(P, b_lo, b_max, target_avg_bits);
+  return hip_status(moe::launch_alloc(gate, P, ns, b_lo, b_max, bits, tau_out, n_hi_out,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_ffn_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T,
+                               int32_t top_k) {
+  moe::FfnShape s;
+  if (ffn_shape(routed, shared, T, top_k, false, &s) != MOE_OK) return 0;
+  return moe::make_layout(s).total;
+}
+
+moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank* shared, const uint16_t* x,
+                           int32_t T, int32_t top_k, const int32_t* topk_idx, const float* topk_gate,
+                           const uint8_t* bits, float* y, int32_t accumulate, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  moe::FfnShape s;
+  moe_status st = ffn_shape(routed, shared, T, top_k, true, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_gate || !bits || !y || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  const moe::FfnLayout L = moe::make_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int ncu = num_cu_cached();
+  moe::MatrixDev none;
+  std::memset(&none, 0, sizeof(none));
+  none.N = 16;
+  none.K = 128;
+  hipError_t e = moe::launch_permute(s, L, ws, topk_idx, bits, strm);
+  if (e == hipSuccess) e = moe::launch_xprep(s, L, ws, x, strm);
+  if (e == hipSuccess)
+    e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = moe::launch_ffn_w2(s, L, ws, w2_of(routed), shared ? w2_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = moe::launch_combine(s, L, ws, topk_gate, y, accumulate, strm);
+  return hip_status(e);
+}
+
+moe_status moe_permute(const int32_t* topk_idx, const uint8_t* bits, int32_t T, int32_t top_k, int32_t E,
+                       int32_t b_max, int32_t* slot_pair, int32_t* expert_offsets, int32_t* expert_maxbits,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || top_k < 1 || top_k > 8 || top_k > E || b_max < 1 || b_max > 4)
+    return MOE_ERR_RANGE;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !bits || !slot_pair || !expert_offsets || !expert_maxbits || !workspace) return MOE_ERR_NULL;
+  if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  const moe::FfnShape s = moe::make_shape(T, top_k, E, b_max, 128, 128, 128, 0, 0);
+  const moe::FfnLayout L = moe::make_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = moe::launch_permute(s, L, ws, topk_idx, bits, strm);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(slot_pair, ws + L.slot_pair, (size_t)s.P * 4, hipMemcpyDeviceToDevice, strm);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(expert_offsets, ws + L.expert_off, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice, strm);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(expert_maxbits, ws + L.expert_maxbits, (size_t)E * 4, hipMemcpyDeviceToDevice, strm);
+  return hip_status(e);
+}
+
+moe_status moe_dequant(const moe_expert_bank* bank, int32_t expert, int32_t matrix, int32_t bits, float* out,
+                       void* stream) {
+  moe_status st = check_bank(bank, true);
+  if (st != MOE_OK) return st;
+  if (expert < 0 || expert >= bank->n_experts || matrix < 0 || matrix > 1 || bits < 1 || bits > bank->b_max)
+    return MOE_ERR_RANGE;
+  if (!out) return MOE_ERR_NULL;
+  const moe::MatrixDev m = matrix == 0 ? w13_of(bank) : w2_of(bank);
+  return hip_status(moe::launch_dequant(m, bank->b_max, bank->group, expert, bits, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* stream) {
+  if (n < 0) return MOE_ERR_RANGE;
+  if (n == 0) return MOE_OK;
+  if (!h || !x) return MOE_ERR_NULL;
+  return hip_status(moe::launch_residual_to_bf16(h, x, n, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Floor-and-compensation dequantisation of one stored matrix (MatMoE review,
+// Core Contribution, F&C paragraph), and the bf16 cast of a residual stream.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+// out[n][c] = fp32(((q >> delta) << delta) + (2^delta - 1)/2 - z) * s, one rounding:
+// the bracket is exact in fp32 (a multiple of 1/2 below 16 in size).
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ planes, const float* __restrict__ sz,
+                                                 int N, int K, int B, int g, int expert, int bits,
+                                                 float* __restrict__ out) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)N * K) return;
+  const int n = (int)(idx / K), c = (int)(idx % K);
+  const size_t plane_words = (size_t)N * K / 32;
+  const int nkb = K >> 7;
+  const int tile = n >> 4, r = n & 15;
+  const int kb = c >> 7, j = (c >> 5) & 3, bit = c & 31;
+  const int quad = kb >> 2;
+  const int nq = min(4, nkb - 4 * quad);
+  const size_t word = (size_t)tile * (K / 2) + 256 * quad + (16 * j + r) * nq + (kb & 3);
+  const uint32_t* base = planes + (size_t)expert * B * plane_words;
+  uint32_t q = 0;
+  for (int p = 0; p < bits; ++p) q = (q << 1) | ((base[p * plane_words + word] >> bit) & 1u);
+  const int delta = B - bits;
+  const float code = (float)(q << delta);
+  const float comp = 0.5f * (float)((1 << delta) - 1);
+  const int NQG = K / g;
+  const float* s = sz + (((size_t)expert * (N >> 4) + tile) * NQG + c / g) * 32;
+  const float scale = s[r], zero = s[16 + r];
+  const float tval = __fadd_rn(__fadd_rn(code, comp), -zero);
+  out[idx] = __fmul_rn(tval, scale);
+}
+
+__global__ __launch_bounds__(256) void k_residual_to_bf16(const float* __restrict__ h, uint16_t* __restrict__ x,
+                                                          int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = (uint16_t)f32_to_bf16(h[i]);
+}
+
+}  // namespace
+
+hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream) {
+  const size_t total = (size_t)m.N * m.K;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(256), 0, stream, m.planes, m.sz, m.N, m.K, B, g, expert, bits,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(k_residual_to_bf16, dim3(blocks), dim3(256), 0, stream, h, x, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router
+size_t route_workspace_bytes(int T, int E);
+hipError_t launch_route(const uint16_t* x, int T, int d, const float* W, int E, const float* bias, int k,
+                        int renorm, int* idx, float* gate, void* ws, hipStream_t stream);
+
+// ---- allocation
+hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_max, uint8_t* bits, float* tau_out,
+                        int* n_hi_out, hipStream_t stream);
+
+// ---- FFN workspace plan
+struct FfnShape {
+  int T, k, E, B, g;     // tokens, top-k, routed experts, b_max, quant group
+  int d, f;              // routed hidden / intermediate
+  int n_shared, fs;      // shared experts and their intermediate size (0 if none)
+  int P, Pt;             // routed pairs, all pairs (routed + shared)
+  int W;                 // 32-token words per bitmap row
+  int max_rchunks;       // routed chunk capacity
+  int n_schunks;         // shared chunks
+  int fmax;              // max(f, fs)
+};
+
+struct FfnLayout {
+  size_t pair_key, bitmap, prefix, slot_pair, pair_slot, slot_info, chunks, meta, expert_off, expert_maxbits;
+  size_t xb, xv, hb, hsum, obuf;
+  size_t total;
+};
+
+FfnShape make_shape(int T, int k, int E, int B, int g, int d, int f, int n_shared, int fs);
+FfnLayout make_layout(const FfnShape& s);
+
+struct MatrixDev {
+  const uint32_t* planes;
+  const float* sz;
+  int N, K;
+};
+
+hipError_t launch_permute(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
+                          hipStream_t stream);
+hipError_t launch_xprep(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream);
+hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
+                          int num_cu, hipStream_t stream);
+hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
+                         int num_cu, hipStream_t stream);
+hipError_t launch_combine(const FfnShape& s, const FfnLayout& L, char* ws, const float* gate, float* y,
+                          int accumulate, hipStream_t stream);
+
+// ---- helpers
+hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream);
+hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream);
+
+}  // namespace moe

@@ -27,8 +27,9 @@ Storage layout of one matrix of one expert, N rows x K columns, B planes
   and bit i of that word is column 128*kb + 32*j + i.  Consecutive k-blocks
   of one (row, chunk) are adjacent, so a 64-lane wave reads a contiguous
   run of 256*nq words with one 16-byte (or 8/12-byte) load per lane.
-* scale/zero: float32 pairs laid out [N/16][K/g][16][2] per expert
-  (tile, quant group, row in tile, (scale, zero)).
+* scale/zero: float32 laid out [N/16][K/g][2][16] per expert (tile, quant
+  group, {scale, zero}, row in tile): the 16 scales of a tile's quant group
+  are contiguous, followed by the 16 zero points.
 """
 from __future__ import annotations
 
@@ -150,10 +151,10 @@ def pack_planes(q: np.ndarray, b_max: int) -> np.ndarray:
 
 
 def pack_scale_zero(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """[E, N, K/g] scale and zero -> float32 [E, N/16, K/g, 16, 2]."""
+    """[E, N, K/g] scale and zero -> float32 [E, N/16, K/g, 2, 16]."""
     E, N, G = s.shape
-    sz = np.stack([s, z], axis=-1).astype(np.float32)                  # [E,N,G,2]
-    sz = sz.reshape(E, N // 16, 16, G, 2).transpose(0, 1, 3, 2, 4)
+    sz = np.stack([s, z], axis=0).astype(np.float32)                   # [2,E,N,G]
+    sz = sz.reshape(2, E, N // 16, 16, G).transpose(1, 2, 4, 0, 3)      # [E,tiles,G,2,16]
     return np.ascontiguousarray(sz)
 
 
@@ -167,9 +168,9 @@ class ExpertBank:
     g: int
     b_max: int
     w13_planes: np.ndarray   # uint32 [E, b_max, words]
-    w13_sz: np.ndarray       # float32 [E, 2f/16, d/g, 16, 2]
+    w13_sz: np.ndarray       # float32 [E, 2f/16, d/g, 2, 16]
     w2_planes: np.ndarray    # uint32 [E, b_max, words]
-    w2_sz: np.ndarray        # float32 [E, d/16, f/g, 16, 2]
+    w2_sz: np.ndarray        # float32 [E, d/16, f/g, 2, 16]
     # codes kept for tests that need the encoder's own view
     q13: Optional[np.ndarray] = None
     q2: Optional[np.ndarray] = None
@@ -320,7 +321,7 @@ def make_stack_layer(cfg: MoeConfig, layer: int) -> tuple:
         G = K // g
         s = (np.float32(0.02 * 5.2 / 15) * (1 + 0.1 * rs.standard_normal((E, N // 16, G, 16)))).astype(np.float32)
         z = rs.integers(6, 10, size=(E, N // 16, G, 16)).astype(np.float32)
-        return np.ascontiguousarray(np.stack([s, z], axis=-1))
+        return np.ascontiguousarray(np.stack([s, z], axis=3))
 
     bank = ExpertBank(E, d, f, g, B, planes(2 * f, d), sz(2 * f, d), planes(d, f), sz(d, f))
     return w_router, bank

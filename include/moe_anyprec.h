@@ -1,0 +1,244 @@
+/*
+ * moe_anyprec.h -- C ABI of libmoe_anyprec.so, a dynamic any-precision
+ * Mixture-of-Experts FFN layer for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer whose expert weights are stored once as most-significant-bit
+ * first bitplanes (up to 4 planes, per-group fp32 scale and zero point) and
+ * read, per (token, expert) pair, at a bit-width chosen at run time from the
+ * live router gate scores.  The steps follow these pages:
+ *   - "DPA-MoE: A Runtime Precision Control Framework for MoE Inference"
+ *     (abstract): prefix-decodable chunks, allocation after routing from
+ *     live gate scores, one checkpoint at many budgets.
+ *   - "MatMoE: Matryoshka Mixture-of-Experts with Dynamic Mixed-Precision
+ *     Quantization for Efficient Inference" (abstract; review, Core
+ *     Contribution): floor-and-compensation reads, a routing-score threshold
+ *     set by binary search to hit a target average bit-width, bitplane
+ *     storage.
+ *   - "DuoRate: Two-Rate Per-Expert Precision Allocation for
+ *     Mixture-of-Experts Serving" (abstract): a decode step pays only for
+ *     the experts it selects; the stream is prefix-readable.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     and allocates every buffer, workspaces included; the library never
+ *     allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *     work is enqueued on it; outputs are valid once the stream completes.
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - The returned status reflects argument validation (done on the host in
+ *     O(1), before any HIP call, so it works on a host without a GPU) and
+ *     launch errors.  Data-dependent contract violations (an expert index
+ *     out of range, a bit-width outside [1, b_max], duplicate experts in one
+ *     token's top-k) never make a kernel read or write out of bounds: such
+ *     pairs are dropped from the output.
+ *   - No C++ exception crosses the ABI.  The library keeps no state between
+ *     calls except a cached device property, so calls are thread-safe; calls
+ *     that share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_ANYPREC_H
+#define MOE_ANYPREC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  MOE_ERR_SHAPE = 2,        /* a size is inconsistent (e.g. d not a multiple of 128) */
+  MOE_ERR_ALIGN = 3,        /* a buffer is not 16-byte aligned                      */
+  MOE_ERR_RANGE = 4,        /* an argument is outside its documented range          */
+  MOE_ERR_WORKSPACE = 5,    /* workspace too small                                  */
+  MOE_ERR_UNSUPPORTED = 6,  /* valid but not supported by this build                */
+  MOE_ERR_HIP = 7           /* a HIP call failed; see moe_last_hip_error()          */
+} moe_status;
+
+/*
+ * One bank of experts (routed or shared), described by a HOST struct whose
+ * pointers are device pointers.  Storage format (the stored checkpoint; "one
+ * encoded checkpoint" of the DPA-MoE abstract, "bitplane storage" of the
+ * MatMoE review, Core Contribution):
+ *
+ *   Matrix W13 of an expert is 2*d_ff x d_model (rows 0..d_ff-1 gate
+ *   projection, rows d_ff..2*d_ff-1 up projection); W2 is d_model x d_ff
+ *   (down projection).  Each weight has an unsigned code q in
+ *   [0, 2^b_max - 1]; plane p (p = 0 first) holds bit b_max-1-p of q.
+ *
+ *   *_planes: uint32 words [E][b_max][N/16 * 16*K/32] for an N x K matrix.
+ *     Plane-major, so the first b planes of a matrix are one contiguous
+ *     prefix.  Within a plane: 16-row tiles of 16*K/32 words each; within a
+ *     tile, for 128-column block kb (K/128 blocks) and 32-column chunk j of
+ *     it, row r of the tile has its word at
+ *         256*(kb/4) + (16*j + r)*nq + kb%4,   nq = min(4, K/128 - 4*(kb/4)),
+ *     and bit i of that word is column 128*kb + 32*j + i.
+ *   *_sz: float32 [E][N/16][K/group][2][16]: for tile, quant group G (columns
+ *     G*group .. G*group+group-1): the scales s of the tile's 16 rows, then
+ *     their zero points z.  z is integer-valued in [0, 2^b_max - 1].  (s, z) is shared by every read
+ *     width ("SharedScale", DPA-MoE abstract; "shared quantization
+ *     parameters", MatMoE review).
+ *
+ *   Reading b planes gives, with delta = b_max - b, the floor-and-compensation
+ *   weight (MatMoE review, Core Contribution, F&C paragraph):
+ *       w = ((q >> delta) * 2^delta + (2^delta - 1)/2 - z) * s.
+ *
+ *   Requirements: 1 <= n_experts; d_model, d_ff multiples of 128; group in
+ *   {64, 128}; 1 <= b_max <= 4; planes and sz 16-byte aligned.
+ */
+typedef struct {
+  int32_t n_experts;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t group;
+  int32_t b_max;
+  const uint32_t* w13_planes;
+  const float* w13_sz;
+  const uint32_t* w2_planes;
+  const float* w2_sz;
+} moe_expert_bank;
+
+/* ------------------------------------------------------------------------ */
+/* Router                                                                    */
+
+/* Workspace bytes moe_route needs for T tokens and E experts (host, pure). */
+size_t moe_route_workspace_bytes(int32_t T, int32_t E);
+
+/*
+ * Router: logits l[t][e] = sum_i W_r[e][i] * x[t][i] (+ logit_bias[e]),
+ * accumulated in float64 from exact bf16/fp32 inputs; softmax over all E
+ * experts; the top_k experts ordered by (logit descending, index
+ * ascending); gate = softmax probability of each chosen expert, divided by
+ * the sum over the chosen k if renorm_topk != 0.  ("routing each token to a
+ * small set of experts", DPA-MoE abstract; "routing scores", MatMoE
+ * abstract.)
+ *   x          [T][d] bf16, 16-byte aligned
+ *   w_router   [E][d] fp32, 16-byte aligned
+ *   logit_bias [E] fp32 or NULL
+ *   topk_idx   [T][top_k] int32 (output)
+ *   topk_gate  [T][top_k] fp32  (output)
+ *   workspace  >= moe_route_workspace_bytes(T, E) bytes, 16-byte aligned,
+ *              zero-filled before its first use; every completed call
+ *              leaves its counters zero again, so it can be reused.
+ * Ranges: T >= 0 (T == 0 is a no-op), d multiple of 128, 1 <= E <= 256,
+ * 1 <= top_k <= min(E, 8).
+ */
+moe_status moe_route(const uint16_t* x, int32_t T, int32_t d, const float* w_router,
+                     int32_t E, const float* logit_bias, int32_t top_k, int32_t renorm_topk,
+                     int32_t* topk_idx, float* topk_gate, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Bit allocation                                                            */
+
+/*
+ * Threshold allocation over the P live routed pairs (MatMoE abstract, item
+ * (3), and review, Core Contribution: pairs whose routing score exceeds a
+ * threshold read high precision, the rest low, the threshold found by binary
+ * search to hit a target average bit-width; DPA-MoE abstract: allocation
+ * after routing from live gate scores).
+ *   n*   = floor(P * (target - b_lo) / (b_max - b_lo)), exact rational
+ *          arithmetic on the float target, clamped to [0, P];
+ *   tau  = the smallest fp32 value with #{gate > tau} <= n*, found on the
+ *          device by bisection over the bit pattern of tau (32 steps);
+ *   bits[i] = b_max if gate[i] > tau, else b_lo.
+ * Equal gate scores are never split: the number of high pairs n_hi is the
+ * largest count a threshold can realise that does not exceed n*.
+ *   gate   [P] fp32 (any order; typically topk_gate viewed as [T*top_k])
+ *   bits   [P] uint8 (output)
+ *   tau_out  fp32 scalar or NULL (output; -inf when every pair is high)
+ *   n_hi_out int32 scalar or NULL (output)
+ * Ranges: P >= 0 (P == 0 is a no-op), 1 <= b_lo <= b_max <= 4,
+ * b_lo <= target <= b_max.  Gates must not be NaN.
+ */
+moe_status moe_alloc_bits(const float* gate, int32_t P, int32_t b_lo, int32_t b_max,
+                          float target_avg_bits, uint8_t* bits, float* tau_out,
+                          int32_t* n_hi_out, void* stream);
+
+/* n* computed on the host exactly as moe_alloc_bits does (pure). */
+int32_t moe_budget_pairs(int32_t P, int32_t b_lo, int32_t b_max, float target_avg_bits);
+
+/* ------------------------------------------------------------------------ */
+/* Any-precision expert FFN                                                  */
+
+/*
+ * Workspace bytes for moe_anyprec_ffn / moe_permute (host, pure).  `shared`
+ * may be NULL.  Returns 0 if the arguments are invalid.
+ */
+size_t moe_ffn_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared,
+                               int32_t T, int32_t top_k);
+
+/*
+ * The layer's expert computation at per-pair bit-widths:
+ *   for every pair (t, j) with e = topk_idx[t][j], b = bits[t*top_k + j]:
+ *     g = W_gate^(b) x_t,  u = W_up^(b) x_t   (fp32 accumulation)
+ *     h = bf16_round(silu(g) * u)             (silu(v) = v / (1 + e^-v))
+ *     o = W_down^(b) h
+ *   y[t] = (accumulate ? y[t] : 0) + sum_j topk_gate[t][j] * o_(t,j)
+ *          + sum_s FFN_shared_s^(b_max)(x_t)     (shared experts, weight 1)
+ * where W^(b) is the floor-and-compensation read of the first b planes.
+ * Each expert's planes are streamed once per group of up to 16 of its
+ * pairs, at the largest width any of those pairs needs; every pair only
+ * uses its own planes (the read is masked per pair), so the result is the
+ * per-pair definition above ("pays only for the experts it selects",
+ * DuoRate abstract; prefix reads, DPA-MoE abstract).
+ *   x          [T][d_model] bf16, 16-byte aligned
+ *   topk_idx   [T][top_k] int32, entries in [0, routed->n_experts), distinct per token
+ *   topk_gate  [T][top_k] fp32
+ *   bits       [T*top_k] uint8 in [1, routed->b_max]
+ *   y          [T][d_model] fp32 (output; read too if accumulate != 0), 16-byte aligned
+ *   workspace  >= moe_ffn_workspace_bytes(...), 256-byte aligned, any content
+ * shared: NULL or a bank with the routed bank's d_model, group and b_max;
+ * all of its n_experts experts are applied to every token at b_max planes.
+ * Ranges: T >= 0 (T == 0 is a no-op), 1 <= top_k <= min(E, 8), E <= 256.
+ */
+moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank* shared,
+                           const uint16_t* x, int32_t T, int32_t top_k,
+                           const int32_t* topk_idx, const float* topk_gate,
+                           const uint8_t* bits, float* y, int32_t accumulate,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The token-to-expert permutation and histogram step of moe_anyprec_ffn, on
+ * its own, for inspection.  Pairs are ordered stably by (expert ascending,
+ * bits descending, pair id ascending), pair id = t*top_k + j.
+ *   slot_pair       [T*top_k] int32 (output): pair id at each sorted position
+ *                   (-1 where a dropped pair left a hole)
+ *   expert_offsets  [E+1] int32 (output): first sorted position of each expert
+ *   expert_maxbits  [E] int32 (output): largest bit-width among the expert's
+ *                   pairs (0 for an expert with no pair)
+ * The workspace is the same as for moe_anyprec_ffn.
+ */
+moe_status moe_permute(const int32_t* topk_idx, const uint8_t* bits, int32_t T, int32_t top_k,
+                       int32_t E, int32_t b_max, int32_t* slot_pair, int32_t* expert_offsets,
+                       int32_t* expert_maxbits, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Helpers                                                                   */
+
+/*
+ * Materialise the floor-and-compensation weights of one matrix of one expert
+ * read at `bits` planes: out[n][c] = fp32(((q>>delta)*2^delta + c_delta - z)*s)
+ * with one rounding (MatMoE review, Core Contribution, F&C paragraph).
+ *   matrix 0 = W13 (out [2*d_ff][d_model]), 1 = W2 (out [d_model][d_ff]).
+ * Ranges: 0 <= expert < n_experts, 1 <= bits <= b_max.
+ */
+moe_status moe_dequant(const moe_expert_bank* bank, int32_t expert, int32_t matrix,
+                       int32_t bits, float* out, void* stream);
+
+/* x[i] = bf16_round_nearest_even(h[i]) for i < n: the next layer's input
+ * from an fp32 residual stream.  n >= 0. */
+moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status status);
+
+/* hipError_t of the last MOE_ERR_HIP returned on the calling thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ANYPREC_H */

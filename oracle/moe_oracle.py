@@ -71,11 +71,16 @@ def unpack_codes(planes: np.ndarray, b_max: int, N: int, K: int) -> np.ndarray:
 
 
 def unpack_scale_zero(sz: np.ndarray, N: int, G: int):
-    """sz float32 [E, N/16, G, 16, 2] -> (scale, zero) float64 [E, N, G]."""
-    sz = np.asarray(sz, dtype=np.float64)
+    """sz float32 [E, N/16, G, 2, 16] (tile, quant group, {scale, zero}, row
+    in tile) -> (scale, zero) float64 [E, N, G]."""
+    sz = np.asarray(sz, dtype=np.float64).reshape(-1, N // 16, G, 2, 16)
     E = sz.shape[0]
-    a = sz.transpose(0, 1, 3, 2, 4).reshape(E, N, G, 2)
-    return a[..., 0].copy(), a[..., 1].copy()
+    scale = np.empty((E, N, G))
+    zero = np.empty((E, N, G))
+    for n in range(N):
+        scale[:, n, :] = sz[:, n // 16, :, 0, n % 16]
+        zero[:, n, :] = sz[:, n // 16, :, 1, n % 16]
+    return scale, zero
 
 
 # ---------------------------------------------------------------------------

@@ -328,8 +328,8 @@ def test_layer_equals_naive_bitwise_loop(tiny):
             for p in range(b):
                 q = q * 2 + _bit_of(planes[e, p], N, K, n, c)
             code = q * 2 ** delta + comp
-            s = float(sz[e, n // 16, c // g, n % 16, 0])
-            z = float(sz[e, n // 16, c // g, n % 16, 1])
+            s = float(sz[e, n // 16, c // g, 0, n % 16])
+            z = float(sz[e, n // 16, c // g, 1, n % 16])
             return (code - z) * s
 
         gu = [sum(weight(bank.w13_planes, bank.w13_sz, 2 * f, d, n, c) * x[t, c] for c in range(d))
