@@ -1,0 +1,293 @@
+"""Benchmark of the dynamic any-precision MoE layer on one MI355X.
+
+Workload: one Qwen3-30B-A3B-shaped MoE layer in decode (hidden 2048, expert
+intermediate 768, 128 experts, top-8, SwiGLU, 4 bitplanes, group 128),
+synthetic seeded inputs.  A step is one pass of the whole layer over a batch:
+router (logits, softmax, top-k), bit allocation (threshold bisection to the
+target average), and the any-precision expert FFN with the gate-weighted
+combine.  Inputs are resident in HBM before timing; four copies of the
+expert bank (1.36 GB) are rotated and eight activation batches cycled so the
+256 MB last-level cache can not serve the weights.
+
+The headline step runs T=32 tokens at target 3.0 bits, replayed from HIP
+graphs; a sweep over T in {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
+The roofline object is for the FFN stage (moe_anyprec_ffn: permutation,
+activation prep, gate/up + SwiGLU, down, combine), timed with HIP events on
+its stream around each call, against the algorithmic bytes of that call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N_COPIES = 4
+N_XBATCH = 8
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_ffn_bytes(idx, bits, cfg, accumulate=False):
+    """Bytes the FFN stage must move: the first b_e planes and the (scale,
+    zero) of every active expert (b_e = widest pair of the expert), the
+    activations in, the output, and the bf16 intermediate round trip."""
+    d, f, g = cfg.d, cfg.f, cfg.g
+    idx = np.asarray(idx).ravel()
+    bits = np.asarray(bits).ravel().astype(np.int64)
+    be = np.zeros(cfg.E, dtype=np.int64)
+    np.maximum.at(be, idx, bits)
+    act = be > 0
+    planes = int(np.sum(be[act])) * 3 * d * f // 8
+    sz = int(np.sum(act)) * 3 * d * f // g * 8
+    T = idx.size // cfg.k
+    io = T * d * 2 + T * d * 4 * (2 if accumulate else 1) + idx.size * f * 2 * 2
+    return planes + sz + io, float(np.mean(be[act])), float(np.mean(bits)), int(np.sum(act))
+
+
+def router_bytes(cfg, T):
+    return cfg.E * cfg.d * 4 + T * cfg.d * 2 + T * cfg.k * 9
+
+
+class Layer:
+    """Device state for one workload: bank copies, x batches, buffers, graphs."""
+
+    def __init__(self, cfg, w, torch, bd, T):
+        self.cfg, self.torch, self.bd, self.T = cfg, torch, bd, T
+        dev = "cuda"
+        base = bd.DeviceBank.from_host(w.routed)
+        self.banks = [base] + [base.clone() for _ in range(N_COPIES - 1)]
+        from dynamic_any_precision_amd import workloads as wl
+        self.xs = [bd.bf16_tensor(wl.step_activations(cfg, s, T)) for s in range(N_XBATCH)]
+        self.wr = torch.from_numpy(w.w_router).to(dev)
+        self.rws = bd.route_workspace(T, cfg.E)
+        self.fws = bd.ffn_workspace(base, None, T, cfg.k)
+        self.idx = [torch.empty(T, cfg.k, dtype=torch.int32, device=dev) for _ in range(N_XBATCH)]
+        self.gate = [torch.empty(T, cfg.k, dtype=torch.float32, device=dev) for _ in range(N_XBATCH)]
+        self.bits = [torch.empty(T * cfg.k, dtype=torch.uint8, device=dev) for _ in range(N_XBATCH)]
+        self.y = torch.empty(T, cfg.d, dtype=torch.float32, device=dev)
+        self.graphs = {}
+
+    def step(self, i, target, ev=None):
+        bd, cfg = self.bd, self.cfg
+        s = i % N_XBATCH
+        bank = self.banks[i % N_COPIES]
+        bd.route(self.xs[s], self.wr, None, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
+        bd.alloc_bits(self.gate[s].view(-1), cfg.b_lo, cfg.b_max, target, bits=self.bits[s])
+        if ev is not None:
+            ev[0].record()
+        bd.anyprec_ffn(bank, None, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
+                       workspace=self.fws)
+        if ev is not None:
+            ev[1].record()
+
+    def capture(self, target):
+        torch = self.torch
+        key = float(target)
+        if key in self.graphs:
+            return self.graphs[key]
+        gs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(N_XBATCH):       # warm the kernels outside capture
+                self.step(i, target)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(N_XBATCH):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(i, target)
+            gs.append(g)
+        torch.cuda.synchronize()
+        self.graphs[key] = gs
+        return gs
+
+    def timed_graph(self, target, steps, warmup):
+        torch = self.torch
+        gs = self.capture(target)
+        for i in range(warmup):
+            gs[i % N_XBATCH].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            gs[i % N_XBATCH].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def timed_events(self, target, steps):
+        """Eager steps; HIP events around each FFN call on the current stream."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(N_XBATCH):
+            self.step(i, target)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step(i, target, evs[i])
+        torch.cuda.synchronize()
+        ffn_ms = [a.elapsed_time(b) for a, b in evs]
+        nbytes, bread, balloc, nact = [], [], [], []
+        for i in range(steps):
+            s = i % N_XBATCH
+            b, br, ba, na = algorithmic_ffn_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg)
+            nbytes.append(b); bread.append(br); balloc.append(ba); nact.append(na)
+        return dict(ffn_ms=float(np.mean(ffn_ms)), ffn_ms_p10=float(np.percentile(ffn_ms, 10)),
+                    ffn_ms_p50=float(np.percentile(ffn_ms, 50)), ffn_ms_p90=float(np.percentile(ffn_ms, 90)),
+                    ffn_bytes=float(np.mean(nbytes)), bits_read=float(np.mean(bread)),
+                    bits_alloc=float(np.mean(balloc)), n_active=float(np.mean(nact)))
+
+
+def cpu_baseline(cfg, w, budget_s=20.0):
+    """The oracle, untouched, on a bounded sample: whole routing and
+    allocation of one T-token batch plus the expert FFN of its first tokens,
+    in one host thread."""
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    done_tokens = 0
+    t0 = time.perf_counter()
+    try:
+        if ctx:
+            ctx.__enter__()
+        rc = orc.bank_cache(w.routed)          # fresh cache: dequantisation is part of the work
+        tok = 0
+        while time.perf_counter() - t0 < budget_s and tok < cfg.T:
+            orc.layer(w.x_bf16, w.w_router, None, cfg.k, cfg.b_lo, cfg.b_max, cfg.target, rc, tokens=[tok])
+            rc = orc.bank_cache(w.routed)
+            tok += 1
+            done_tokens += 1
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    return dict(value=done_tokens / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done_tokens} token(s) of the T={cfg.T} batch: full routing and allocation of the batch "
+                       f"plus those tokens' 8 expert FFNs (dequantised from the stored planes), float64 NumPy, "
+                       f"{el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--target", type=float, default=3.0)
+    ap.add_argument("--tokens", type=int, default=32)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device-to-device copy of MIB MiB (a reference dispatch of known "
+                         "size for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer runs on a single MI355X and has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dynamic_any_precision_amd import binding as bd
+    from dynamic_any_precision_amd import workloads as wl
+    bd.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_calibration} MiB device copies")
+        del src, dst
+
+    cfg = wl.config(2, T=args.tokens, target=args.target)
+    log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
+    t0 = time.perf_counter()
+    w = wl.make_workload(cfg, keep_codes=False)
+    log(f"generated in {time.perf_counter() - t0:.1f} s; stored {w.routed.stored_bytes() / 1e6:.1f} MB per copy")
+
+    layers = {}
+
+    def layer_for(T):
+        if T not in layers:
+            layers[T] = Layer(cfg, w, torch, bd, T)
+        return layers[T]
+
+    T = args.tokens
+    L = layer_for(T)
+    log(f"timing T={T} target={args.target}: {args.warmup} warmup + {args.steps} graph-replayed steps")
+    t_step = L.timed_graph(args.target, args.steps, args.warmup)
+    log(f"step {t_step * 1e3:.4f} ms; event-timing the FFN stage")
+    ev = L.timed_events(args.target, args.steps)
+    achieved = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
+    step_bytes = ev["ffn_bytes"] + router_bytes(cfg, T)
+
+    sweep = []
+    if not args.no_sweep:
+        for TT in (1, 32):
+            LT = layer_for(TT)
+            for tgt in (2.0, 2.5, 3.0, 4.0):
+                n = max(20, args.steps // 4)
+                ts = LT.timed_graph(tgt, n, 5)
+                e2 = LT.timed_events(tgt, n)
+                gbs = e2["ffn_bytes"] / (e2["ffn_ms"] * 1e-3) / 1e9
+                sweep.append(dict(T=TT, target=tgt, tokens_per_s=TT / ts, ms_per_step=ts * 1e3,
+                                  ffn_ms=e2["ffn_ms"], ffn_gbs=gbs, ffn_frac=gbs / HBM_PEAK_GBS,
+                                  bits_read=e2["bits_read"], bits_alloc=e2["bits_alloc"],
+                                  n_active=e2["n_active"], ffn_bytes=e2["ffn_bytes"]))
+                log(f"sweep T={TT} target={tgt}: {TT / ts:.0f} tok/s, FFN {e2['ffn_ms'] * 1e3:.1f} us, "
+                    f"{gbs:.0f} GB/s, bits read {e2['bits_read']:.2f}")
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, w)
+
+    out = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s vs avg bits read (Qwen3-30B shape)",
+        "value": T / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer, decode", "tokens": T, "hidden": cfg.d,
+                   "expert_intermediate": cfg.f, "experts": cfg.E, "top_k": cfg.k, "bitplanes": cfg.b_max,
+                   "group": cfg.g, "b_lo": cfg.b_lo, "target_avg_bits": args.target,
+                   "weight_copies_rotated": N_COPIES, "activation_batches": N_XBATCH},
+        "step_gbs": step_bytes / t_step / 1e9,
+        "bits_read": ev["bits_read"],
+        "bits_alloc": ev["bits_alloc"],
+        "n_active_experts": ev["n_active"],
+        "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "moe_anyprec_ffn (permute, xprep, w13+SwiGLU, w2, combine)",
+                     "bytes_per_launch": ev["ffn_bytes"]},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,11 +3,12 @@
 // batch meets a target average bit-width; DPA-MoE abstract: allocation after
 // routing from live gate scores).
 //
-// One block.  Gate scores are mapped to order-preserving 32-bit keys and held
-// in registers; tau is built from its most significant bit down: bit b of the
-// answer is 0 iff #{key > prefix | (2^b - 1)} <= n*, which makes tau the
-// smallest key whose strict upper set fits the budget.  32 steps, each one
-// block-wide count.
+// One block (one wave when P <= 2048).  Gate scores are mapped to
+// order-preserving 32-bit keys and held in registers; tau is built from its
+// most significant bit down: bit b of the answer is 0 iff
+// #{key > prefix | (2^b - 1)} <= n*, which makes tau the smallest key whose
+// strict upper set fits the budget.  32 steps, each one count reduced with
+// DPP lane moves (plus one LDS exchange between waves for large P).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,7 +16,6 @@ namespace moe {
 
 namespace {
 
-constexpr int AL_VPT = 32;  // keys per thread kept in registers
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -29,7 +29,7 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 
 template <int NT>
 __device__ __forceinline__ int block_count(int c, int* red) {
-  c = wave_sum_i(c);
+  c = wave_sum_i_dpp(c);
   if constexpr (NT == WAVE) {
     return c;
   } else {
@@ -44,7 +44,7 @@ __device__ __forceinline__ int block_count(int c, int* red) {
   }
 }
 
-template <int NT>
+template <int NT, int AL_VPT>
 __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, int P, int n_star, int b_lo,
                                               int b_max, uint8_t* __restrict__ bits, float* __restrict__ tau_out,
                                               int* __restrict__ n_hi_out) {
@@ -90,12 +90,15 @@ __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, in
 
 hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_max, uint8_t* bits, float* tau_out,
                         int* n_hi_out, hipStream_t stream) {
-  if (P <= WAVE * AL_VPT) {
-    hipLaunchKernelGGL(k_alloc<WAVE>, dim3(1), dim3(WAVE), 0, stream, gate, P, n_star, b_lo, b_max, bits, tau_out,
-                       n_hi_out);
+  if (P <= WAVE * 4) {
+    hipLaunchKernelGGL((k_alloc<WAVE, 4>), dim3(1), dim3(WAVE), 0, stream, gate, P, n_star, b_lo, b_max, bits,
+                       tau_out, n_hi_out);
+  } else if (P <= WAVE * 32) {
+    hipLaunchKernelGGL((k_alloc<WAVE, 32>), dim3(1), dim3(WAVE), 0, stream, gate, P, n_star, b_lo, b_max, bits,
+                       tau_out, n_hi_out);
   } else {
-    hipLaunchKernelGGL(k_alloc<1024>, dim3(1), dim3(1024), 0, stream, gate, P, n_star, b_lo, b_max, bits, tau_out,
-                       n_hi_out);
+    hipLaunchKernelGGL((k_alloc<1024, 32>), dim3(1), dim3(1024), 0, stream, gate, P, n_star, b_lo, b_max, bits,
+                       tau_out, n_hi_out);
   }
   return hipGetLastError();
 }

@@ -37,6 +37,19 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// Wave-wide integer sum through DPP lane moves (no LDS round trips):
+// quad swaps, half-row and row mirrors give every lane its 16-lane row sum,
+// row broadcasts 15 and 31 carry the rows into lane 63.
+__device__ __forceinline__ int wave_sum_i_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
@@ -56,13 +69,15 @@ __device__ __forceinline__ double wave_max_d(double v) {
 // (bit i = column i of the chunk).  A unit of one or two consecutive planes
 // (p, p+1) is turned into 16 words of packed bf16 pairs; output word k
 // (k = 0..15) carries column k in its low half and column k+16 in its high
-// half, each as the bf16 value 128 + f * 4^a(k), where f = 2*bit_p + bit_{p+1}
-// is the unit's 2-bit field of that column and a(k) = (k/2) mod 3.  Placing
-// the field at mantissa offset 2*a(k) lets every output word be produced by a
-// single shift-free AND-OR from one of three pre-shifted sources, so a 32-column
-// chunk costs 24 ALU operations per unit.  The activations that meet word k
-// are pre-scaled by 4^-a(k), and the constant 128 is removed afterwards
-// through the group sums, so the products sum to exactly sum_c f(c) x(c).
+// half, each as the bf16 value 2^e (128 + f * 4^a(k)), where f = 2*bit_p +
+// bit_{p+1} is the unit's 2-bit field of that column (bit_{p+1} = 0 for a
+// one-plane unit), a(k) = (k/2) mod 3 and 2^e the unit's place value
+// (e = b_max - 2 - p), carried by the exponent field of the bias constant.
+// Placing the field at mantissa offset 2*a(k) lets every output word be made
+// by one AND-OR from one of three pre-shifted sources: 24 ALU operations per
+// unit and chunk.  The activations that meet word k are pre-scaled by
+// 4^-a(k); the constant 2^e * 128 is removed afterwards through the group
+// sums, so the products sum to exactly sum_c 2^e f(c) x(c).
 //
 // MFMA i (i = 0..3) takes output words 4i..4i+3; in the bf16 16x16x32 operand
 // layout a lane's 8 K-slots are then (word 4i+u, half h) -> slot 2u+h, i.e.
@@ -71,55 +86,65 @@ __device__ __forceinline__ double wave_max_d(double v) {
 __host__ __device__ constexpr int a_exp(int k) { return (k >> 1) % 3; }
 
 // Position of chunk column c (0..31) inside the B-fragment of its chunk:
-// returns mfma index i in bits [4:3] and the slot in bits [2:0].
+// mfma index i in bits [4:3], slot in bits [2:0].
 __host__ __device__ constexpr int frag_pos(int c) {
   return (((c & 15) >> 2) << 3) | (((c & 3) << 1) | (c >> 4));
 }
 
-struct Frag16 {
-  uint32_t w[16];
-};
-
-__device__ __forceinline__ void unpack_unit(uint32_t hi, uint32_t lo, Frag16& o) {
-  // Even columns: field of column 2m at bits 2m..2m+1; odd columns likewise.
-  const uint32_t E0 = ((hi << 1) & 0xAAAAAAAAu) | (lo & 0x55555555u);
-  const uint32_t O0 = (hi & 0xAAAAAAAAu) | ((lo >> 1) & 0x55555555u);
-  const uint32_t E6 = E0 >> 6, E12 = E0 >> 12;
-  const uint32_t O6 = O0 >> 6, O12 = O0 >> 12;
-  const uint32_t B = 0x43004300u;
-  o.w[0] = (E0 & 0x00030003u) | B;
-  o.w[1] = (O0 & 0x00030003u) | B;
-  o.w[2] = (E0 & 0x000C000Cu) | B;
-  o.w[3] = (O0 & 0x000C000Cu) | B;
-  o.w[4] = (E0 & 0x00300030u) | B;
-  o.w[5] = (O0 & 0x00300030u) | B;
-  o.w[6] = (E6 & 0x00030003u) | B;
-  o.w[7] = (O6 & 0x00030003u) | B;
-  o.w[8] = (E6 & 0x000C000Cu) | B;
-  o.w[9] = (O6 & 0x000C000Cu) | B;
-  o.w[10] = (E6 & 0x00300030u) | B;
-  o.w[11] = (O6 & 0x00300030u) | B;
-  o.w[12] = (E12 & 0x00030003u) | B;
-  o.w[13] = (O12 & 0x00030003u) | B;
-  o.w[14] = (E12 & 0x000C000Cu) | B;
-  o.w[15] = (O12 & 0x000C000Cu) | B;
+// bf16 pair bias 2^e * 128 in both halves.
+__host__ __device__ constexpr uint32_t unit_bias(int e) {
+  return (uint32_t)((134 + e) << 7) * 0x10001u;
 }
 
-__device__ __forceinline__ bf16x8_t frag_operand(const Frag16& f, int i) {
-  bf16x8_t v;
-  uint32_t* p = reinterpret_cast<uint32_t*>(&v);
-  p[0] = f.w[4 * i + 0];
-  p[1] = f.w[4 * i + 1];
-  p[2] = f.w[4 * i + 2];
-  p[3] = f.w[4 * i + 3];
-  return v;
-}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
+// (x & m) | c in one VALU op; m and c live in VGPRs.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
   return r;
 }
+
+struct UnpackConst {
+  uint32_t m0, m1, m2;  // field masks at offsets 0, 2, 4 in both halves
+};
+
+// Materialise a constant in a VGPR once (opaque to rematerialisation).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+__device__ __forceinline__ UnpackConst unpack_const() {
+  UnpackConst k;
+  k.m0 = vconst(0x00030003u);
+  k.m1 = vconst(0x000C000Cu);
+  k.m2 = vconst(0x00300030u);
+  return k;
+}
+
+// Four MFMA A operands (words 4i..4i+3 each) of one unit.
+__device__ __forceinline__ void unpack_unit(uint32_t hi, uint32_t lo, bool two, uint32_t bias, UnpackConst k,
+                                            u32x4_t (&o)[4]) {
+  uint32_t E0, O0;
+  if (two) {
+    E0 = ((hi << 1) & 0xAAAAAAAAu) | (lo & 0x55555555u);
+    O0 = (hi & 0xAAAAAAAAu) | ((lo >> 1) & 0x55555555u);
+  } else {
+    E0 = (hi << 1) & 0xAAAAAAAAu;
+    O0 = hi & 0xAAAAAAAAu;
+  }
+  const uint32_t E6 = E0 >> 6, E12 = E0 >> 12;
+  const uint32_t O6 = O0 >> 6, O12 = O0 >> 12;
+  o[0] = u32x4_t{and_or(E0, k.m0, bias), and_or(O0, k.m0, bias), and_or(E0, k.m1, bias), and_or(O0, k.m1, bias)};
+  o[1] = u32x4_t{and_or(E0, k.m2, bias), and_or(O0, k.m2, bias), and_or(E6, k.m0, bias), and_or(O6, k.m0, bias)};
+  o[2] = u32x4_t{and_or(E6, k.m1, bias), and_or(O6, k.m1, bias), and_or(E6, k.m2, bias), and_or(O6, k.m2, bias)};
+  o[3] = u32x4_t{and_or(E12, k.m0, bias), and_or(O12, k.m0, bias), and_or(E12, k.m1, bias), and_or(O12, k.m1, bias)};
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ u32x4_t as_u32x4(uint4 v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

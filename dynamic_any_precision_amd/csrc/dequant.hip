@@ -16,12 +16,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ pl
   if (idx >= (size_t)N * K) return;
   const int n = (int)(idx / K), c = (int)(idx % K);
   const size_t plane_words = (size_t)N * K / 32;
-  const int nkb = K >> 7;
   const int tile = n >> 4, r = n & 15;
   const int kb = c >> 7, j = (c >> 5) & 3, bit = c & 31;
-  const int quad = kb >> 2;
-  const int nq = min(4, nkb - 4 * quad);
-  const size_t word = (size_t)tile * (K / 2) + 256 * quad + (16 * j + r) * nq + (kb & 3);
+  const size_t word = (size_t)tile * (K / 2) + 64 * kb + 16 * j + r;
   const uint32_t* base = planes + (size_t)expert * B * plane_words;
   uint32_t q = 0;
   for (int p = 0; p < bits; ++p) q = (q << 1) | ((base[p * plane_words + word] >> bit) & 1u);

@@ -12,19 +12,19 @@
 // f = 2 bit_p + bit_{p+1} (a single plane p uses f = 2 bit_p).
 //
 // Each unit runs on the bf16 matrix cores: 16 rows x 32 columns of a unit
-// become an exact bf16 A operand (values 128 + f 4^a, see common.hpp), the
-// activations, pre-scaled by 2^(B-2-p) 4^-a and masked to the pairs that
-// read that unit, are the B operand, and v_mfma_f32_16x16x32_bf16 sums them
-// in fp32.  Per quant group the fp32 partial is multiplied by s; the
+// become an exact bf16 A operand (values 2^(B-2-p) (128 + f 4^a), see
+// common.hpp), the activations, pre-scaled by 4^-a and masked to the pairs
+// that read that unit, are the B operand, and v_mfma_f32_16x16x32_bf16 sums
+// them in fp32.  Per quant group the fp32 partial is multiplied by s; the
 // remaining terms s * (c_delta X_G - 128 F_t V_G) - s z X_G (V_G the
 // 4^-a-weighted group sum, F_t the sum of the unit factors the pair reads)
 // are two small fp32 products over groups, done with v_mfma_f32_16x16x4f32.
 //
-// Work items: (chunk of <= 16 pairs of one expert, tile pair).  W13: gate
-// rows 16i.. and up rows f+16i.. of the expert; W2: rows 32i..32i+31.  A
-// wave streams the chunk's planes for its two tiles once, in 128-bit loads
-// from the lane-interleaved layout, and serves all pairs of the chunk; a pair
-// only receives the units its own width covers.
+// Work items, one per 256-thread block: (chunk of <= 16 pairs of one expert,
+// row block).  W13: gate rows 32i..32i+31 and the matching up rows; W2:
+// rows 64i..64i+63.  Each wave streams one 16-row tile of the chunk's planes
+// once, in 128-bit loads from the lane-interleaved layout, and serves all
+// pairs of the chunk; a pair only receives the units its own width covers.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -63,9 +63,9 @@ FfnLayout make_layout(const FfnShape& s) {
   L.meta = take(64);
   L.expert_off = take((size_t)(s.E + 1) * 4);
   L.expert_maxbits = take((size_t)s.E * 4);
-  L.xb = take((size_t)s.T * s.B * s.d * 2);
+  L.xb = take((size_t)s.T * s.d * 2);
   L.xv = take((size_t)s.T * (s.d / s.g) * 8);
-  L.hb = take((size_t)s.Pt * s.B * s.fmax * 2);
+  L.hb = take((size_t)s.Pt * s.fmax * 2);
   L.hsum = take((size_t)s.Pt * (s.fmax / 16) * 8);
   L.obuf = take((size_t)s.Pt * s.d * 4);
   L.total = o;
@@ -73,62 +73,6 @@ FfnLayout make_layout(const FfnShape& s) {
 }
 
 namespace {
-
-// ---------------------------------------------------------------------------
-// activation prep: B-fragment order, per-plane scaling, group sums
-
-__global__ __launch_bounds__(64) void k_xprep(const uint16_t* __restrict__ x, int d, int B, int g,
-                                              uint16_t* __restrict__ xb, float2* __restrict__ xv) {
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int nchunk = d / 32;
-  const int cpg = g / 32;  // chunks per quant group
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int ch = c0 + lane;
-    float X = 0.f, V = 0.f;
-    if (ch < nchunk) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d + ch * 32);
-      uint32_t in[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = src[q];
-        in[4 * q + 0] = v.x; in[4 * q + 1] = v.y; in[4 * q + 2] = v.z; in[4 * q + 3] = v.w;
-      }
-      float xf[32];
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        xf[c] = bf16_to_f32((c & 1) ? (in[c >> 1] >> 16) : (in[c >> 1] & 0xFFFFu));
-        X += xf[c];
-        V += xf[c] * (1.0f / (float)(1 << (2 * a_exp(c & 15))));
-      }
-      for (int p = 0; p < B; ++p) {
-        const float pscale = ldexpf(1.0f, B - 2 - p);
-        uint16_t out[32];
-#pragma unroll
-        for (int c = 0; c < 32; ++c) {
-          const float v = xf[c] * pscale * (1.0f / (float)(1 << (2 * a_exp(c & 15))));
-          out[frag_pos(c)] = (uint16_t)f32_to_bf16(v);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(xb + ((size_t)t * B + p) * d + ch * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint4 v;
-          v.x = out[8 * q + 0] | ((uint32_t)out[8 * q + 1] << 16);
-          v.y = out[8 * q + 2] | ((uint32_t)out[8 * q + 3] << 16);
-          v.z = out[8 * q + 4] | ((uint32_t)out[8 * q + 5] << 16);
-          v.w = out[8 * q + 6] | ((uint32_t)out[8 * q + 7] << 16);
-          dst[q] = v;
-        }
-      }
-    }
-    // group sums over cpg consecutive chunks (lanes)
-    for (int m = 1; m < cpg; m <<= 1) {
-      X += __shfl_xor(X, m, WAVE);
-      V += __shfl_xor(V, m, WAVE);
-    }
-    if (ch < nchunk && (lane % cpg) == 0) xv[(size_t)t * (d / g) + ch / cpg] = make_float2(X, V);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // plane units of a chunk, from the set of widths it holds (bit b-1 = width b)
@@ -162,20 +106,24 @@ __host__ __device__ constexpr int mask_bmax(int mask) {
   return (mask & 8) ? 4 : (mask & 4) ? 3 : (mask & 2) ? 2 : 1;
 }
 
+__host__ __device__ constexpr int mask_bmin(int mask) {
+  return (mask & 1) ? 1 : (mask & 2) ? 2 : (mask & 4) ? 3 : 4;
+}
+
 constexpr int MODE_W13 = 0;
 constexpr int MODE_W2 = 1;
 
 struct FfnArgs {
   MatrixDev m[2];        // [0] routed, [1] shared
-  int tpi[2];            // tile pairs per chunk
+  int slices[2];         // work items (16-row tiles) per chunk
   int B, g, T, P, d, fmax;
   const int4* chunks;
   const int* meta;
   int max_rchunks, n_schunks;
   const int* slot_info;
-  const uint16_t* xb;    // W13 B source [T][B][d]
+  const uint16_t* xb;    // W13 B source [T][d]
   const float2* xv;      // [T][d/g]
-  uint16_t* hb;          // [Pt][B][fmax]
+  uint16_t* hb;          // W2 B source [Pt][fmax]
   float2* hsum;          // [Pt][fmax/16]
   float* obuf;           // [Pt][d]
 };
@@ -198,23 +146,37 @@ __device__ __forceinline__ uint32_t comp(const uint4& v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
 }
 
+// ---------------------------------------------------------------------------
+// Streaming core.
+//
+// One wave = one work item (chunk of <= 16 pairs of one expert, 16-row
+// tile).  The wave streams the tile's planes one 128-column k-block at a
+// time (one 32-bit word per lane and plane, 256 contiguous bytes per wave),
+// reads the chunk's activation B-fragments and the tile's scales from L2 one
+// k-block ahead, and keeps little state, so that many waves share each SIMD
+// and hide one another's latencies (no LDS, no barriers).  For gate/up the wave streams the gate tile and then the up
+// tile of the same rows and applies SwiGLU.
+
+constexpr int FFN_THREADS = 256;
+#ifndef FFN_WPE
+#define FFN_WPE 2  // waves per SIMD the kernel is compiled for
+#endif
+
 template <int MODE, int QPK, int MASK>
-__device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, int e, int s0, int m, int ti,
-                                         int is_shared) {
+__device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, int e, int s0, int m, int unit) {
   constexpr Units U = make_units(MASK);
   constexpr int BM = mask_bmax(MASK);
+  constexpr int GPQ = 4 * QPK;  // quant groups per quad
   const int lane = threadIdx.x & 63;
-  const int tcol = lane & 15;  // token column of this lane (B operand, C layout)
-  const int jg = lane >> 4;    // K chunk of this lane (A/B operand) and row quad (C layout)
+  const int tcol = lane & 15;  // token column (B operand, C layout)
+  const int jg = lane >> 4;    // K chunk (A/B operand), row quad (C layout)
   const int B = a.B;
   const int K = M.K;
   const int NKB = K >> 7;
   const int NQ = (NKB + 3) >> 2;
   const int NQG = K / a.g;
   const size_t plane_words = (size_t)M.N * K / 32;
-  const int tile_words = K / 2;
 
-  // token of this lane's column
   int slot = -1, tok = 0, bt = 0;
   if (tcol < m) {
     slot = s0 + tcol;
@@ -222,226 +184,216 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
     tok = info & 0xFFFFFF;
     bt = info >> 24;
   }
-  bool cov[4];
+  // Unit coverage is monotone in the plane index: once a pair stops covering
+  // a unit it covers none of the later ones, so the B operand is masked in
+  // place as the units advance.
+  uint32_t umask[4];
+  uint32_t ubias[4];
   float Ft = 0.f;
 #pragma unroll
   for (int u = 0; u < U.n; ++u) {
-    cov[u] = bt >= U.p[u] + U.np[u];
-    if (cov[u]) Ft += ldexpf(1.0f, B - 2 - U.p[u]);
+    const bool cov = bt >= U.p[u] + U.np[u];
+    umask[u] = cov ? 0xFFFFFFFFu : 0u;
+    ubias[u] = vconst(unit_bias(B - 2 - U.p[u]));
+    if (cov) Ft += ldexpf(1.0f, B - 2 - U.p[u]);
   }
   const float ct = bt > 0 ? 0.5f * (ldexpf(1.0f, B - bt) - 1.0f) : 0.f;
+  const UnpackConst kc = unpack_const();
+  const bool bval = bt > 0;
+  const uint4* bsrc = reinterpret_cast<const uint4*>(
+      MODE == MODE_W13 ? a.xb + (size_t)tok * K + jg * 32 : a.hb + (size_t)(slot < 0 ? 0 : slot) * a.fmax + jg * 32);
+  const int tpg = a.g >> 4;
 
-  // tiles of this work item
-  int tr[2];
-  if (MODE == MODE_W13) {
-    tr[0] = ti;
-    tr[1] = (M.N >> 5) + ti;  // up rows start at f = N/2
-  } else {
-    tr[0] = 2 * ti;
-    tr[1] = 2 * ti + 1;
-  }
-  const uint32_t* pbase[2];
-  const float* szb[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    pbase[r] = M.planes + (size_t)e * B * plane_words + (size_t)tr[r] * tile_words;
-    szb[r] = M.sz + ((size_t)e * (M.N >> 4) + tr[r]) * NQG * 32;
-  }
-  // B-operand source of this lane
-  const uint16_t* bsrc;
-  if (MODE == MODE_W13) {
-    bsrc = a.xb + (size_t)tok * B * K;
-  } else {
-    bsrc = a.hb + (size_t)(slot < 0 ? 0 : slot) * B * a.fmax;
-  }
-  const size_t bstride = (MODE == MODE_W13) ? (size_t)K : (size_t)a.fmax;
+  constexpr int TPU = (MODE == MODE_W13) ? 2 : 1;
+  const float* szexp = M.sz + (size_t)e * (M.N >> 4) * NQG * 32;
+  const uint32_t* pexp = M.planes + (size_t)e * B * plane_words + lane;
+  auto tile_of = [&](int which) { return (MODE == MODE_W13) ? (which == 0 ? unit : (M.N >> 5) + unit) : unit; };
 
-  f32x4_t out[2];
+  // operands of one k-block: one plane word per plane, 4 x 16 B of
+  // activation fragment, the scales of the lane's four C-layout rows
+  struct Ops {
+    uint32_t w[BM];
+    uint4 b[4];
+    float4 s[QPK];
+  };
+  // the k-blocks of the item's tiles form one stream of TPU*NKB steps
+  auto load = [&](int j, Ops& o) {
+    const int which = (TPU == 1) ? 0 : j / NKB;
+    const int kb = j - which * NKB;
+    const int tile = tile_of(which);
+    const uint32_t* pb = pexp + (size_t)tile * (K / 2) + 64 * kb;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) out[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wq[2][BM];
-  {
-    const int nq = min(4, NKB);
+    for (int p = 0; p < BM; ++p) o.w[p] = pb[p * plane_words];
+    if (bval) {
+      const uint4* bp = bsrc + kb * 16;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+      for (int i = 0; i < 4; ++i) o.b[i] = bp[i];
+    } else {
 #pragma unroll
-      for (int p = 0; p < BM; ++p) wq[r][p] = load_words(pbase[r] + p * plane_words + lane * nq, nq);
-  }
-
-  for (int q = 0; q < NQ; ++q) {
-    const int nq = min(4, NKB - 4 * q);
-    uint4 wn[2][BM];
-    if (q + 1 < NQ) {
-      const int nq1 = min(4, NKB - 4 * (q + 1));
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int p = 0; p < BM; ++p)
-          wn[r][p] = load_words(pbase[r] + p * plane_words + 256 * (q + 1) + lane * nq1, nq1);
+      for (int i = 0; i < 4; ++i) o.b[i] = make_uint4(0, 0, 0, 0);
     }
+    const float* szt = szexp + (size_t)tile * NQG * 32;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w < nq) {
-        const int kb = 4 * q + w;
-        f32x4_t acc[QPK][2];
+    for (int h = 0; h < QPK; ++h)
+      o.s[h] = *reinterpret_cast<const float4*>(szt + (size_t)(kb * QPK + h) * 32 + 4 * jg);
+  };
+
+  f32x4_t out = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t gres = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float cs[QPK], cz[QPK], cX[QPK], cV[QPK];
+
+  // correction operands of the 4*QPK groups of k-blocks kb0..kb0+3 of a tile
+  // (lane k-index jg <-> group)
+  auto load_corr = [&](int which, int kb0) {
+    const float* szt = szexp + (size_t)tile_of(which) * NQG * 32;
 #pragma unroll
-        for (int h = 0; h < QPK; ++h)
-#pragma unroll
-          for (int r = 0; r < 2; ++r) acc[h][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < U.n; ++u) {
-          uint4 bv[4];
-          if (cov[u]) {
-            const uint4* src =
-                reinterpret_cast<const uint4*>(bsrc + (size_t)U.p[u] * bstride + kb * 128 + jg * 32);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = src[i];
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = make_uint4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const uint32_t hi = comp(wq[r][U.p[u]], w);
-            const uint32_t lo = (U.np[u] == 2) ? comp(wq[r][U.p[u] + 1], w) : 0u;
-            Frag16 A;
-            unpack_unit(hi, lo, A);
-#pragma unroll
-            for (int h = 0; h < QPK; ++h) {
-              const bool keep = (QPK == 1) || ((jg >> 1) == h);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint4 bb = keep ? bv[i] : make_uint4(0, 0, 0, 0);
-                acc[h][r] = mfma_bf16(frag_operand(A, i), as_bf16x8(bb), acc[h][r]);
-              }
-            }
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < QPK; ++h) {
-          const int G = kb * QPK + h;
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const float4 s4 = *reinterpret_cast<const float4*>(szb[r] + (size_t)G * 32 + 4 * jg);
-            out[r][0] += s4.x * acc[h][r][0];
-            out[r][1] += s4.y * acc[h][r][1];
-            out[r][2] += s4.z * acc[h][r][2];
-            out[r][3] += s4.w * acc[h][r][3];
+    for (int h = 0; h < QPK; ++h) {
+      const int G = kb0 * QPK + 4 * h + jg;
+      const bool gv = G < NQG;
+      cs[h] = gv ? szt[(size_t)G * 32 + tcol] : 0.f;
+      cz[h] = gv ? szt[(size_t)G * 32 + 16 + tcol] : 0.f;
+      cX[h] = 0.f;
+      cV[h] = 0.f;
+      if (gv && bt > 0) {
+        if (MODE == MODE_W13) {
+          const float2 v = a.xv[(size_t)tok * NQG + G];
+          cX[h] = v.x;
+          cV[h] = v.y;
+        } else {
+          const float4* hs =
+              reinterpret_cast<const float4*>(a.hsum + (size_t)slot * (a.fmax >> 4) + (size_t)G * tpg);
+          for (int pt = 0; pt < tpg / 2; ++pt) {
+            const float4 hv = hs[pt];
+            cX[h] += hv.x + hv.z;
+            cV[h] += hv.y + hv.w;
           }
         }
       }
     }
-    if (q + 1 < NQ) {
+  };
+  auto apply_corr = [&]() {
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int p = 0; p < BM; ++p) wq[r][p] = wn[r][p];
+    for (int h = 0; h < QPK; ++h) {
+      const float Kc = ct * cX[h] - 128.0f * Ft * cV[h];
+      corr = mfma_f32(cs[h], Kc, corr);
+      corr = mfma_f32(-cs[h] * cz[h], cX[h], corr);
     }
-  }
+  };
 
-  // group-sum corrections: s*(c X - 128 F V) - s z X, as fp32 matrix products over groups
-  f32x4_t corr[2];
+  auto compute = [&](Ops& o) {
+    f32x4_t acc[QPK];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) corr[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int q4 = 0; q4 < NQG; q4 += 4) {
-    const int G = q4 + jg;
-    const bool gv = G < NQG;
-    float X = 0.f, V = 0.f;
-    if (gv && bt > 0) {
-      if (MODE == MODE_W13) {
-        const float2 v = a.xv[(size_t)tok * NQG + G];
-        X = v.x;
-        V = v.y;
-      } else {
-        const int tpg = a.g >> 4;  // 16-row partials per quant group
-        const float2* hs = a.hsum + (size_t)slot * (a.fmax >> 4) + (size_t)G * tpg;
-        for (int pt = 0; pt < tpg; ++pt) {
-          const float2 v = hs[pt];
-          X += v.x;
-          V += v.y;
+    for (int h = 0; h < QPK; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U.n; ++u) {
+      if (u > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o.b[i].x &= umask[u]; o.b[i].y &= umask[u]; o.b[i].z &= umask[u]; o.b[i].w &= umask[u];
+        }
+      }
+      const uint32_t hi = o.w[U.p[u]];
+      const uint32_t lo = (U.np[u] == 2) ? o.w[U.p[u] + 1] : 0u;
+      u32x4_t A[4];
+      unpack_unit(hi, lo, U.np[u] == 2, ubias[u], kc, A);
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) {
+        const bool keep = (QPK == 1) || ((jg >> 1) == h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t bb = keep ? as_u32x4(o.b[i]) : u32x4_t{0u, 0u, 0u, 0u};
+          acc[h] = mfma_bf16(as_bf16x8(A[i]), as_bf16x8(bb), acc[h]);
         }
       }
     }
-    const float Kc = ct * X - 128.0f * Ft * V;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      float sv = 0.f, zv = 0.f;
-      if (gv) {
-        sv = szb[r][(size_t)G * 32 + tcol];
-        zv = szb[r][(size_t)G * 32 + 16 + tcol];
-      }
-      corr[r] = mfma_f32(sv, Kc, corr[r]);
-      corr[r] = mfma_f32(-sv * zv, X, corr[r]);
+    for (int h = 0; h < QPK; ++h) {
+      out[0] += o.s[h].x * acc[h][0];
+      out[1] += o.s[h].y * acc[h][1];
+      out[2] += o.s[h].z * acc[h][2];
+      out[3] += o.s[h].w * acc[h][3];
     }
-  }
+  };
 
-  if (MODE == MODE_W13) {
-    const int f = M.N >> 1;
-    const size_t hstride = (size_t)a.fmax;
-    float Xp = 0.f, Vp = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float gval = out[0][i] + corr[0][i];
-      const float uval = out[1][i] + corr[1][i];
-      const float hval = gval / (1.0f + expf(-gval)) * uval;
-      const uint32_t hb16 = f32_to_bf16(hval);
-      const float hf = bf16_to_f32(hb16);
-      const int n = ti * 16 + 4 * jg + i;  // column of W2
-      const float ainv = 1.0f / (float)(1 << (2 * a_exp(n & 15)));
-      Xp += hf;
-      Vp += hf * ainv;
-      if (bt > 0) {
-        const int pos = (n & ~31) + frag_pos(n & 31);
-#pragma unroll
-        for (int u = 0; u < U.n; ++u) {
-          if (cov[u]) {
-            const float v = hf * ldexpf(1.0f, B - 2 - U.p[u]) * ainv;
-            a.hb[((size_t)slot * B + U.p[u]) * hstride + pos] = (uint16_t)f32_to_bf16(v);
-          }
-        }
+  auto finish_tile = [&](int which) {
+    const f32x4_t res = out + corr;
+    out = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (MODE == MODE_W13) {
+      if (which == 0) {
+        gres = res;
+        return;
       }
-    }
-    (void)f;
-    Xp += __shfl_xor(Xp, 16, WAVE);
-    Vp += __shfl_xor(Vp, 16, WAVE);
-    Xp += __shfl_xor(Xp, 32, WAVE);
-    Vp += __shfl_xor(Vp, 32, WAVE);
-    if (jg == 0 && bt > 0) a.hsum[(size_t)slot * (a.fmax >> 4) + ti] = make_float2(Xp, Vp);
-  } else {
-    if (bt > 0) {
+      float Xp = 0.f, Vp = 0.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        float4 o;
-        o.x = out[r][0] + corr[r][0];
-        o.y = out[r][1] + corr[r][1];
-        o.z = out[r][2] + corr[r][2];
-        o.w = out[r][3] + corr[r][3];
-        *reinterpret_cast<float4*>(a.obuf + (size_t)slot * a.d + tr[r] * 16 + 4 * jg) = o;
+      for (int i = 0; i < 4; ++i) {
+        const float gval = gres[i];
+        const float hval = gval / (1.0f + expf(-gval)) * res[i];
+        const float hf = bf16_to_f32(f32_to_bf16(hval));
+        const int n = unit * 16 + 4 * jg + i;  // column of W2
+        const float ainv = 1.0f / (float)(1 << (2 * a_exp(n & 15)));
+        Xp += hf;
+        Vp += hf * ainv;
+        if (bt > 0) a.hb[(size_t)slot * a.fmax + (n & ~31) + frag_pos(n & 31)] = (uint16_t)f32_to_bf16(hf * ainv);
       }
+      Xp += __shfl_xor(Xp, 16, WAVE);
+      Vp += __shfl_xor(Vp, 16, WAVE);
+      Xp += __shfl_xor(Xp, 32, WAVE);
+      Vp += __shfl_xor(Vp, 32, WAVE);
+      if (jg == 0 && bt > 0) a.hsum[(size_t)slot * (a.fmax >> 4) + unit] = make_float2(Xp, Vp);
+    } else {
+      if (bt > 0)
+        *reinterpret_cast<float4*>(a.obuf + (size_t)slot * a.d + unit * 16 + 4 * jg) =
+            make_float4(res[0], res[1], res[2], res[3]);
     }
+  };
+
+  // One stream step: issue the loads PF k-blocks ahead into the ring slot
+  // freed by the previous step, then compute this k-block; corrections at
+  // every fourth k-block of a tile and at its end.
+  constexpr int PF = 3;
+  const int NJ = TPU * NKB;
+  auto step = [&](int j, Ops& cur, Ops& ahead) {
+    if (j + PF < NJ) load(j + PF, ahead);
+    const int which = (TPU == 1) ? 0 : j / NKB;
+    const int kb = j - which * NKB;
+    if ((kb & 3) == 0) load_corr(which, kb);
+    compute(cur);
+    if ((kb & 3) == 3 || kb == NKB - 1) apply_corr();
+    if (kb == NKB - 1) finish_tile(which);
+  };
+
+  Ops o0, o1, o2, o3;
+  load(0, o0);
+  if (1 < NJ) load(1, o1);
+  if (2 < NJ) load(2, o2);
+  for (int j = 0; j < NJ; j += 4) {
+    step(j, o0, o3);
+    if (j + 1 < NJ) step(j + 1, o1, o0);
+    if (j + 2 < NJ) step(j + 2, o2, o1);
+    if (j + 3 < NJ) step(j + 3, o3, o2);
   }
-  (void)is_shared;
 }
 
 template <int MODE, int QPK>
-__global__ __launch_bounds__(256) void k_ffn(FfnArgs a) {
+__global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN_WPE, FFN_WPE))) void k_ffn(FfnArgs a) {
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nw = (gridDim.x * blockDim.x) >> 6;
   const int n_rc = a.meta[0];
-  const long items_r = (long)n_rc * a.tpi[0];
-  const long items = items_r + (long)a.n_schunks * a.tpi[1];
+  const long items_r = (long)n_rc * a.slices[0];
+  const long items = items_r + (long)a.n_schunks * a.slices[1];
   for (long w = gw; w < items; w += nw) {
     int4 ch;
-    int ti, sh;
+    int unit, sh;
     if (w < items_r) {
-      ch = a.chunks[w / a.tpi[0]];
-      ti = (int)(w % a.tpi[0]);
+      ch = a.chunks[w / a.slices[0]];
+      unit = (int)(w % a.slices[0]);
       sh = 0;
     } else {
       const long w2 = w - items_r;
-      ch = a.chunks[a.max_rchunks + w2 / a.tpi[1]];
-      ti = (int)(w2 % a.tpi[1]);
+      ch = a.chunks[a.max_rchunks + w2 / a.slices[1]];
+      unit = (int)(w2 % a.slices[1]);
       sh = 1;
     }
     const MatrixDev& M = a.m[sh];
@@ -449,7 +401,7 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a) {
     switch (mask) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_item<MODE, QPK, MK>(a, M, ch.x, ch.y, ch.z, ti, sh); \
+    run_item<MODE, QPK, MK>(a, M, ch.x, ch.y, ch.z, unit); \
     break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
       MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
@@ -503,49 +455,47 @@ FfnArgs make_args(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev rou
   return a;
 }
 
-int grid_for(long max_items, int num_cu) {
-  const long waves = max_items;
-  long blocks = (waves + 3) / 4;
-  const long cap = (long)num_cu * 8;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  return (int)blocks;
+hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
+                      int num_cu, hipStream_t stream) {
+  FfnArgs a = make_args(s, L, ws, routed, shared);
+  // work items per chunk: gate/up -> f/16 tile rows, down -> d/16
+  if (mode == MODE_W13) {
+    a.slices[0] = s.f / 16;
+    a.slices[1] = s.n_shared ? s.fs / 16 : 1;
+  } else {
+    a.slices[0] = s.d / 16;
+    a.slices[1] = s.d / 16;
+  }
+  const int qpk = (s.g == 64) ? 2 : 1;
+  const long max_items = (long)s.max_rchunks * a.slices[0] + (long)s.n_schunks * a.slices[1];
+  long grid = (max_items + 3) / 4;
+  const long cap = (long)num_cu * FFN_WPE;  // FFN_WPE waves per SIMD x 4 SIMDs / 4 waves per block
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (mode == MODE_W13) {
+    if (qpk == 2)
+      hipLaunchKernelGGL((k_ffn<MODE_W13, 2>), dim3(grid), dim3(FFN_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_ffn<MODE_W13, 1>), dim3(grid), dim3(FFN_THREADS), 0, stream, a);
+  } else {
+    if (qpk == 2)
+      hipLaunchKernelGGL((k_ffn<MODE_W2, 2>), dim3(grid), dim3(FFN_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_ffn<MODE_W2, 1>), dim3(grid), dim3(FFN_THREADS), 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_xprep(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream) {
-  hipLaunchKernelGGL(k_xprep, dim3(s.T), dim3(64), 0, stream, x, s.d, s.B, s.g,
-                     reinterpret_cast<uint16_t*>(ws + L.xb), reinterpret_cast<float2*>(ws + L.xv));
-  return hipGetLastError();
-}
-
 hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
                           int num_cu, hipStream_t stream) {
-  FfnArgs a = make_args(s, L, ws, routed, shared);
-  a.tpi[0] = s.f / 16;
-  a.tpi[1] = s.n_shared ? s.fs / 16 : 1;
-  const long max_items = (long)s.max_rchunks * a.tpi[0] + (long)s.n_schunks * a.tpi[1];
-  const int grid = grid_for(max_items, num_cu);
-  if (s.g == 64)
-    hipLaunchKernelGGL((k_ffn<MODE_W13, 2>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_ffn<MODE_W13, 1>), dim3(grid), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_ffn(MODE_W13, s, L, ws, routed, shared, num_cu, stream);
 }
 
 hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
                          int num_cu, hipStream_t stream) {
-  FfnArgs a = make_args(s, L, ws, routed, shared);
-  a.tpi[0] = s.d / 32;
-  a.tpi[1] = s.d / 32;
-  const long max_items = (long)(s.max_rchunks + s.n_schunks) * a.tpi[0];
-  const int grid = grid_for(max_items, num_cu);
-  if (s.g == 64)
-    hipLaunchKernelGGL((k_ffn<MODE_W2, 2>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_ffn<MODE_W2, 1>), dim3(grid), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_ffn(MODE_W2, s, L, ws, routed, shared, num_cu, stream);
 }
 
 hipError_t launch_combine(const FfnShape& s, const FfnLayout& L, char* ws, const float* gate, float* y,

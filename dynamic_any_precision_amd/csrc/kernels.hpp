@@ -43,9 +43,10 @@ struct MatrixDev {
   int N, K;
 };
 
-hipError_t launch_permute(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
-                          hipStream_t stream);
-hipError_t launch_xprep(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream);
+// Plan (permutation, histogram, chunks) plus, when x is given, the activation
+// fragments of every token.
+hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
+                       const uint16_t* x, hipStream_t stream);
 hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
                           int num_cu, hipStream_t stream);
 hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,

@@ -2,12 +2,15 @@
 // in one launch.  ("routing each token to a small set of experts",
 // DPA-MoE abstract; "routing scores", MatMoE abstract.)
 //
-// Grid (E/16 expert tiles, T/8 token tiles), 256 threads.  Each wave owns 4
-// experts of the tile and accumulates 4 x 8 (expert, token) dot products in
-// float64 over its slice of the hidden dimension; a butterfly
-// reduce-scatter leaves lane l with the full sum of pair l mod 32.  The last block
+// Grid (E/8 expert tiles, T/8 token tiles), 256 threads.  The four waves of a
+// block split the hidden dimension; each accumulates the 8 x 8 (expert,
+// token) dot products of its slice in float64 from exact bf16 / fp32
+// inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
+// pair l, and wave 0 adds the four slices in a fixed order.  The last block
 // of a token tile to finish (atomic counter, reset afterwards) runs softmax
-// and top-k for the tile's tokens, one wave per token.
+// and top-k for the tile's tokens, one wave per token: every lane ranks the
+// experts it owns against all logits of the token, (logit desc, index asc),
+// so the top k are found without serial rounds.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,12 +18,12 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_TT = 8;   // tokens per block
-constexpr int RT_EW = 4;   // experts per wave
-constexpr int RT_ET = 16;  // experts per block
+constexpr int RT_TT = 8;  // tokens per block
+constexpr int RT_ET = 8;  // experts per block
+constexpr int RT_WAVES = 4;
 
 template <int M>
-__device__ __forceinline__ void butterfly_step(double (&v)[32], int lane) {
+__device__ __forceinline__ void butterfly_step(double (&v)[64], int lane) {
   const bool up = (lane & M) != 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
@@ -31,69 +34,71 @@ __device__ __forceinline__ void butterfly_step(double (&v)[32], int lane) {
   if constexpr (M > 1) butterfly_step<M / 2>(v, lane);
 }
 
-// Full sum across the two wave halves, then a reduce-scatter: after the step
-// with mask M, v[0 .. M-1] hold partial sums of the indices selected by the
-// lane's higher bits; finally v[0] = total of index lane % 32.
-__device__ __forceinline__ void butterfly32(double (&v)[32], int lane) {
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] += __shfl_xor(v[i], 32, WAVE);
-  butterfly_step<16>(v, lane);
-}
+// Reduce-scatter: after the step with mask M, v[0 .. M-1] hold partial sums
+// of the indices selected by the lane's higher bits; finally v[0] is the
+// wave total of index `lane`.
+__device__ __forceinline__ void butterfly64(double (&v)[64], int lane) { butterfly_step<32>(v, lane); }
 
 __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, int T, int d,
                                                const float* __restrict__ W, int E,
                                                const float* __restrict__ bias, int k, int renorm,
                                                int* __restrict__ idx_out, float* __restrict__ gate_out,
                                                double* __restrict__ logits, unsigned* __restrict__ counters) {
+  __shared__ double part[RT_WAVES][64];
+  __shared__ double tl[RT_WAVES][256];
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.y * RT_TT;
   const int nt = min(RT_TT, T - t0);
-  const int e0 = blockIdx.x * RT_ET + wave * RT_EW;
+  const int e0 = blockIdx.x * RT_ET;
+  const int slice = ((d / RT_WAVES) + 3) & ~3;
+  const int c_beg = wave * slice;
+  const int c_end = min(d, c_beg + slice);
 
-  double acc[32];
+  double acc[64];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.0;
+  for (int i = 0; i < 64; ++i) acc[i] = 0.0;
 
-  for (int c = lane * 4; c < d; c += 256) {
-    double w[RT_EW][4];
+  for (int c = c_beg + lane * 4; c < c_end; c += 256) {
+    float4 wv[RT_ET];
 #pragma unroll
-    for (int ee = 0; ee < RT_EW; ++ee) {
-      float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + ee < E) wv = *reinterpret_cast<const float4*>(W + (size_t)(e0 + ee) * d + c);
-      w[ee][0] = wv.x; w[ee][1] = wv.y; w[ee][2] = wv.z; w[ee][3] = wv.w;
-    }
+    for (int ee = 0; ee < RT_ET; ++ee)
+      wv[ee] = (e0 + ee < E) ? *reinterpret_cast<const float4*>(W + (size_t)(e0 + ee) * d + c)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint2 xv[RT_TT];
+#pragma unroll
+    for (int tt = 0; tt < RT_TT; ++tt)
+      xv[tt] = (tt < nt) ? *reinterpret_cast<const uint2*>(x + (size_t)(t0 + tt) * d + c) : make_uint2(0, 0);
 #pragma unroll
     for (int tt = 0; tt < RT_TT; ++tt) {
-      if (tt < nt) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + tt) * d + c);
-        const double x0 = bf16_to_f32(xv.x & 0xFFFFu), x1 = bf16_to_f32(xv.x >> 16);
-        const double x2 = bf16_to_f32(xv.y & 0xFFFFu), x3 = bf16_to_f32(xv.y >> 16);
+      const double x0 = bf16_to_f32(xv[tt].x & 0xFFFFu), x1 = bf16_to_f32(xv[tt].x >> 16);
+      const double x2 = bf16_to_f32(xv[tt].y & 0xFFFFu), x3 = bf16_to_f32(xv[tt].y >> 16);
 #pragma unroll
-        for (int ee = 0; ee < RT_EW; ++ee) {
-          double a = acc[ee * RT_TT + tt];
-          a = fma(w[ee][0], x0, a);
-          a = fma(w[ee][1], x1, a);
-          a = fma(w[ee][2], x2, a);
-          a = fma(w[ee][3], x3, a);
-          acc[ee * RT_TT + tt] = a;
-        }
+      for (int ee = 0; ee < RT_ET; ++ee) {
+        double a = acc[ee * RT_TT + tt];
+        a = fma((double)wv[ee].x, x0, a);
+        a = fma((double)wv[ee].y, x1, a);
+        a = fma((double)wv[ee].z, x2, a);
+        a = fma((double)wv[ee].w, x3, a);
+        acc[ee * RT_TT + tt] = a;
       }
     }
   }
-  butterfly32(acc, lane);
-  if (lane < 32) {
+  butterfly64(acc, lane);
+  part[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave == 0) {
     const int ee = lane / RT_TT, tt = lane % RT_TT;
     const int e = e0 + ee, t = t0 + tt;
     if (e < E && tt < nt) {
-      double l = acc[0];
+      double l = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
       if (bias) l += (double)bias[e];
       logits[(size_t)t * E + e] = l;
     }
   }
 
   // ---- last block of this token tile: softmax + top-k ----
-  __shared__ int s_last;
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -104,65 +109,62 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
   if (!s_last) return;
   __threadfence();
 
-  for (int tt = wave; tt < nt; tt += 4) {
-    const int t = t0 + tt;
-    const volatile double* lrow = logits + (size_t)t * E;
-    double lv[4];
-    double m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      lv[i] = (e < E) ? lrow[e] : -INFINITY;
-      m = fmax(m, lv[i]);
+  // every wave runs the same number of rounds, so the barriers are uniform
+  for (int round = 0; round < RT_TT / RT_WAVES; ++round) {
+    const int tt = wave + round * RT_WAVES;
+    const bool active = tt < nt;
+    const int t = t0 + (active ? tt : 0);
+    if (active)
+      for (int e = lane; e < E; e += 64)
+        tl[wave][e] = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (!active) {
+      __syncthreads();
+      continue;
     }
-    m = wave_max_d(m);
-    double ps = 0.0;
-    double pv[4];
+    double lv[4];
+    int rank[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      lv[i] = -INFINITY;
+      rank[i] = 0x7FFFFFFF;
       const int e = lane + 64 * i;
-      pv[i] = (e < E) ? exp(lv[i] - m) : 0.0;
+      if (e < E) {
+        lv[i] = tl[wave][e];
+        int r = 0;
+#pragma unroll 16
+        for (int o = 0; o < E; ++o) {
+          const double lo = tl[wave][o];
+          r += (lo > lv[i] || (lo == lv[i] && o < e)) ? 1 : 0;
+        }
+        rank[i] = r;
+      }
+    }
+    double mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmax(mx, lv[i]);
+    mx = wave_max_d(mx);
+    double ps = 0.0, pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = (lane + 64 * i < E) ? exp(lv[i] - mx) : 0.0;
       ps += pv[i];
     }
     ps = wave_sum_d(ps);
-    // top-k by (logit desc, index asc); lane r keeps the r-th choice
-    bool taken[4] = {false, false, false, false};
-    double my_g = 0.0;
-    int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-      double bv = -INFINITY;
-      int be = 0x7FFFFFFF;
+    double pk = 0.0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !taken[i] && (lv[i] > bv || (lv[i] == bv && e < be))) { bv = lv[i]; be = e; }
-      }
+    for (int i = 0; i < 4; ++i)
+      if (rank[i] < k) pk += pv[i] / ps;
+    const double gsum = renorm ? wave_sum_d(pk) : 1.0;
 #pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const double ov = __shfl_xor(bv, msk, WAVE);
-        const int oe = __shfl_xor(be, msk, WAVE);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      // probability of the winner, broadcast from its owner lane
-      double p = 0.0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (lane + 64 * i == be) {
-          taken[i] = true;
-          p = pv[i];
-        }
-      }
-      p = wave_sum_d(p) / ps;
-      if (lane == r) {
-        my_g = p;
-        my_i = be;
+    for (int i = 0; i < 4; ++i) {
+      if (rank[i] < k) {
+        const double p = pv[i] / ps;
+        idx_out[(size_t)t * k + rank[i]] = lane + 64 * i;
+        gate_out[(size_t)t * k + rank[i]] = (float)(renorm ? p / gsum : p);
       }
     }
-    const double gsum = wave_sum_d(lane < k ? my_g : 0.0);
-    if (lane < k) {
-      idx_out[(size_t)t * k + lane] = my_i;
-      gate_out[(size_t)t * k + lane] = (float)(renorm ? my_g / gsum : my_g);
-    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) counters[blockIdx.y] = 0u;
 }

@@ -21,12 +21,11 @@ Storage layout of one matrix of one expert, N rows x K columns, B planes
   each split into four 32-column chunks j = 0..3.  The word holding row
   n = 16*tile + r, k-block kb, chunk j sits at
 
-      tile_base + 256*(kb // 4) + (16*j + r) * nq + (kb % 4),
-      nq = min(4, K/128 - 4*(kb // 4)),
+      tile * (16*K/32) + 64*kb + (16*j + r),
 
-  and bit i of that word is column 128*kb + 32*j + i.  Consecutive k-blocks
-  of one (row, chunk) are adjacent, so a 64-lane wave reads a contiguous
-  run of 256*nq words with one 16-byte (or 8/12-byte) load per lane.
+  and bit i of that word is column 128*kb + 32*j + i.  A 64-lane wave reads
+  one k-block of one tile as 256 contiguous bytes, lane 16*j + r holding the
+  32 columns that lane needs for the matrix-core operand.
 * scale/zero: float32 laid out [N/16][K/g][2][16] per expert (tile, quant
   group, {scale, zero}, row in tile): the 16 scales of a tile's quant group
   are contiguous, followed by the 16 zero points.
@@ -132,22 +131,15 @@ def pack_planes(q: np.ndarray, b_max: int) -> np.ndarray:
     assert N % 16 == 0 and K % 128 == 0
     nkb = K // 128
     tiles = N // 16
-    out = np.empty((E, b_max, tiles, 16 * K // 32), dtype=np.uint32)
+    out = np.empty((E, b_max, tiles * 16 * K // 32), dtype=np.uint32)
     for p in range(b_max):
         bits = ((q >> (b_max - 1 - p)) & 1).astype(np.uint8)          # [E, N, K]
-        # [E, tiles, r, kb, j, i]
-        bits = bits.reshape(E, tiles, 16, nkb, 4, 32)
-        words = np.packbits(bits, axis=-1, bitorder="little")          # [E,tiles,r,kb,j,4 bytes]
-        words = np.ascontiguousarray(words).view("<u4")[..., 0]         # [E,tiles,r,kb,j]
-        parts = []
-        for qd in range((nkb + 3) // 4):
-            kb0 = 4 * qd
-            nq = min(4, nkb - kb0)
-            blk = words[:, :, :, kb0:kb0 + nq, :]                       # [E,tiles,r,nq,j]
-            blk = blk.transpose(0, 1, 4, 2, 3)                          # [E,tiles,j,r,nq] -> lane=16j+r
-            parts.append(blk.reshape(E, tiles, 64 * nq))
-        out[:, p] = np.concatenate(parts, axis=-1)
-    return out.reshape(E, b_max, tiles * 16 * K // 32)
+        bits = bits.reshape(E, tiles, 16, nkb, 4, 32)                   # [E, tiles, r, kb, j, i]
+        words = np.packbits(bits, axis=-1, bitorder="little")          # [E, tiles, r, kb, j, 4 bytes]
+        words = np.ascontiguousarray(words).view("<u4")[..., 0]         # [E, tiles, r, kb, j]
+        words = words.transpose(0, 1, 3, 4, 2)                          # [E, tiles, kb, j, r]
+        out[:, p] = words.reshape(E, -1)
+    return out
 
 
 def pack_scale_zero(s: np.ndarray, z: np.ndarray) -> np.ndarray:

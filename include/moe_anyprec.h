@@ -71,9 +71,8 @@ typedef enum {
  *     Plane-major, so the first b planes of a matrix are one contiguous
  *     prefix.  Within a plane: 16-row tiles of 16*K/32 words each; within a
  *     tile, for 128-column block kb (K/128 blocks) and 32-column chunk j of
- *     it, row r of the tile has its word at
- *         256*(kb/4) + (16*j + r)*nq + kb%4,   nq = min(4, K/128 - 4*(kb/4)),
- *     and bit i of that word is column 128*kb + 32*j + i.
+ *     it, row r of the tile has its word at  64*kb + 16*j + r,  and bit i of
+ *     that word is column 128*kb + 32*j + i.
  *   *_sz: float32 [E][N/16][K/group][2][16]: for tile, quant group G (columns
  *     G*group .. G*group+group-1): the scales s of the tile's 16 rows, then
  *     their zero points z.  z is integer-valued in [0, 2^b_max - 1].  (s, z) is shared by every read

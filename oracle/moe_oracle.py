@@ -39,18 +39,14 @@ def plane_word_and_bit(n, c, N: int, K: int):
 
     Layout (the stored format; [MAT] Core Contribution, bitplane storage):
     rows in tiles of 16, columns in 128-column blocks of four 32-column
-    chunks; the words of one (row, chunk) for up to four consecutive blocks
-    are adjacent.  Works elementwise on NumPy integer arrays."""
-    nkb = K // 128
+    chunks; within a tile, block-major, then chunk, then row.  Works
+    elementwise on NumPy integer arrays."""
     tile = n // 16
     r = n % 16
     kb = c // 128
     j = (c % 128) // 32
     bit = c % 32
-    quad = kb // 4
-    nq = np.minimum(4, nkb - 4 * quad)
-    lane = 16 * j + r
-    word = tile * (16 * K // 32) + 256 * quad + lane * nq + (kb % 4)
+    word = tile * (16 * K // 32) + 64 * kb + 16 * j + r
     return word, bit
 
 

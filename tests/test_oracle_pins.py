@@ -304,11 +304,8 @@ def _bit_of(planes_e_p, N, K, n, c):
     tile, r = divmod(n, 16)
     kb, rem = divmod(c, 128)
     j, i = divmod(rem, 32)
-    nkb = K // 128
-    quad = kb // 4
-    nq = min(4, nkb - 4 * quad)
     tile_words = 16 * K // 32
-    word = tile * tile_words + quad * 64 * 4 + (16 * j + r) * nq + kb % 4
+    word = tile * tile_words + kb * 64 + j * 16 + r
     return (int(planes_e_p[word]) >> i) & 1
 
 
