@@ -183,7 +183,8 @@ moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank*
   std::memset(&none, 0, sizeof(none));
   none.N = 16;
   none.K = 128;
-  hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, x, strm);
+  hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
+  if (e == hipSuccess) e = moe::launch_gather(s, L, ws, x, strm);
   if (e == hipSuccess)
     e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
   if (e == hipSuccess) e = moe::launch_ffn_w2(s, L, ws, w2_of(routed), shared ? w2_of(shared) : none, ncu, strm);
@@ -204,7 +205,7 @@ moe_status moe_permute(const int32_t* topk_idx, const uint8_t* bits, int32_t T, 
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, nullptr, strm);
+  hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
   if (e == hipSuccess)
     e = hipMemcpyAsync(slot_pair, ws + L.slot_pair, (size_t)s.P * 4, hipMemcpyDeviceToDevice, strm);
   if (e == hipSuccess)

@@ -98,12 +98,10 @@ __host__ __device__ constexpr uint32_t unit_bias(int e) {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// (x & m) | c in one VALU op; m and c live in VGPRs.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
-  return r;
-}
+// (x & m) | c: one v_and_or_b32 with m and c in VGPRs.  Written in plain C so
+// that the compiler sees the instruction: its results feed matrix-core
+// operands, and the wait states between the two are the compiler's to insert.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
 struct UnpackConst {
   uint32_t m0, m1, m2;  // field masks at offsets 0, 2, 4 in both halves

@@ -30,7 +30,7 @@ struct FfnShape {
 
 struct FfnLayout {
   size_t pair_key, bitmap, prefix, slot_pair, pair_slot, slot_info, chunks, meta, expert_off, expert_maxbits;
-  size_t xb, xv, hb, hsum, obuf;
+  size_t xg, xvg, hg, hsg, obuf;  // chunk activation fragments and sums, gate/up output, down output
   size_t total;
 };
 
@@ -43,10 +43,11 @@ struct MatrixDev {
   int N, K;
 };
 
-// Plan (permutation, histogram, chunks) plus, when x is given, the activation
-// fragments of every token.
+// Plan: permutation, histogram, chunks.
 hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
-                       const uint16_t* x, hipStream_t stream);
+                       hipStream_t stream);
+// Activation fragments of every chunk (after the plan).
+hipError_t launch_gather(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream);
 hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,
                           int num_cu, hipStream_t stream);
 hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,

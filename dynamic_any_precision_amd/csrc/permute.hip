@@ -48,54 +48,6 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return base + incl - v;
 }
 
-// ---------------------------------------------------------------------------
-// activation prep (one wave per token): B-fragment order, 4^-a scaling and
-// the plain and 4^-a-weighted sums of every quant group.
-
-__device__ void xprep_token(const uint16_t* __restrict__ x, int t, int d, int g, uint16_t* __restrict__ xb,
-                            float2* __restrict__ xv) {
-  const int lane = threadIdx.x & 63;
-  const int nchunk = d / 32;
-  const int cpg = g / 32;  // chunks per quant group
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int ch = c0 + lane;
-    float X = 0.f, V = 0.f;
-    if (ch < nchunk) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d + ch * 32);
-      uint32_t in[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = src[q];
-        in[4 * q + 0] = v.x; in[4 * q + 1] = v.y; in[4 * q + 2] = v.z; in[4 * q + 3] = v.w;
-      }
-      uint16_t out[32];
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const float xf = bf16_to_f32((c & 1) ? (in[c >> 1] >> 16) : (in[c >> 1] & 0xFFFFu));
-        const float sc = 1.0f / (float)(1 << (2 * a_exp(c & 15)));
-        X += xf;
-        V += xf * sc;
-        out[frag_pos(c)] = (uint16_t)f32_to_bf16(xf * sc);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(xb + (size_t)t * d + ch * 32);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint4 v;
-        v.x = out[8 * q + 0] | ((uint32_t)out[8 * q + 1] << 16);
-        v.y = out[8 * q + 2] | ((uint32_t)out[8 * q + 3] << 16);
-        v.z = out[8 * q + 4] | ((uint32_t)out[8 * q + 5] << 16);
-        v.w = out[8 * q + 6] | ((uint32_t)out[8 * q + 7] << 16);
-        dst[q] = v;
-      }
-    }
-    for (int m = 1; m < cpg; m <<= 1) {
-      X += __shfl_xor(X, m, WAVE);
-      V += __shfl_xor(V, m, WAVE);
-    }
-    if (ch < nchunk && (lane % cpg) == 0) xv[(size_t)t * (d / g) + ch / cpg] = make_float2(X, V);
-  }
-}
-
 struct PlanPtrs {
   int* pair_key;
   uint32_t* bitmap;
@@ -228,23 +180,15 @@ __device__ void permute_body(const FfnShape& s, const PlanPtrs& pp, const int* _
   for (int i = tid; i < s.n_shared * s.T; i += PM_NT) pp.slot_info[P + i] = (i % s.T) | (B << 24);
 }
 
-// Block 0 builds the plan; blocks 1.. prepare the activations of 16 tokens
-// each (independent of the plan).
 __global__ __launch_bounds__(PM_NT) void k_plan(FfnShape s, PlanPtrs pp, const int* __restrict__ idx,
-                                                const uint8_t* __restrict__ bits, const uint16_t* __restrict__ x,
-                                                uint16_t* __restrict__ xb, float2* __restrict__ xv) {
-  if (blockIdx.x == 0) {
-    permute_body(s, pp, idx, bits);
-    return;
-  }
-  const int t = (blockIdx.x - 1) * (PM_NT / WAVE) + (threadIdx.x >> 6);
-  if (t < s.T) xprep_token(x, t, s.d, s.g, xb, xv);
+                                                const uint8_t* __restrict__ bits) {
+  permute_body(s, pp, idx, bits);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
-                       const uint16_t* x, hipStream_t stream) {
+                       hipStream_t stream) {
   PlanPtrs pp;
   pp.pair_key = reinterpret_cast<int*>(ws + L.pair_key);
   pp.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
@@ -256,9 +200,7 @@ hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const in
   pp.meta = reinterpret_cast<int*>(ws + L.meta);
   pp.expert_off = reinterpret_cast<int*>(ws + L.expert_off);
   pp.expert_maxbits = reinterpret_cast<int*>(ws + L.expert_maxbits);
-  const int xblocks = x ? (s.T + PM_NT / WAVE - 1) / (PM_NT / WAVE) : 0;
-  hipLaunchKernelGGL(k_plan, dim3(1 + xblocks), dim3(PM_NT), 0, stream, s, pp, idx, bits, x,
-                     reinterpret_cast<uint16_t*>(ws + L.xb), reinterpret_cast<float2*>(ws + L.xv));
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(PM_NT), 0, stream, s, pp, idx, bits);
   return hipGetLastError();
 }
 

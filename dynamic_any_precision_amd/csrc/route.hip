@@ -8,9 +8,8 @@
 // inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
 // pair l, and wave 0 adds the four slices in a fixed order.  The last block
 // of a token tile to finish (atomic counter, reset afterwards) runs softmax
-// and top-k for the tile's tokens, one wave per token: every lane ranks the
-// experts it owns against all logits of the token, (logit desc, index asc),
-// so the top k are found without serial rounds.
+// and top-k for the tile's tokens, one wave per token: k rounds of a
+// wave-wide arg-max over (logit desc, index asc).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,6 +37,81 @@ __device__ __forceinline__ void butterfly_step(double (&v)[64], int lane) {
 // of the indices selected by the lane's higher bits; finally v[0] is the
 // wave total of index `lane`.
 __device__ __forceinline__ void butterfly64(double (&v)[64], int lane) { butterfly_step<32>(v, lane); }
+
+// Order-preserving map of a double to an unsigned 64-bit key (larger logit,
+// larger key; -0 and +0 equal).  Logits are finite.
+__device__ __forceinline__ uint64_t order_key64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// (key, index) a beats (key, index) b: larger logit, then smaller index.
+__device__ __forceinline__ bool beats(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Softmax over the E logits of one token and its top k, by one wave: k
+// rounds of a wave-wide arg-max over (logit desc, index asc); lane l owns
+// experts l, l+64, l+128, l+192.
+__device__ void topk_token(const double* __restrict__ tl, int E, int k, int renorm, int* __restrict__ idx_out,
+                           float* __restrict__ gate_out, int lane) {
+  double lv[4];
+  uint64_t key[4];
+  bool avail[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    avail[i] = e < E;
+    lv[i] = avail[i] ? tl[e] : 0.0;
+    key[i] = avail[i] ? order_key64(lv[i]) : 0ull;
+  }
+  double mx = 0.0, ps = 0.0, psel = 0.0;
+  int my_e = 0;        // lane r keeps the winner of round r
+  double my_l = 0.0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t bk = 0ull;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (avail[i] && beats(key[i], lane + 64 * i, bk, be)) {
+        bk = key[i];
+        be = lane + 64 * i;
+      }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)bk, m, WAVE);
+      const uint32_t hi = __shfl_xor((uint32_t)(bk >> 32), m, WAVE);
+      const int oe = __shfl_xor(be, m, WAVE);
+      const uint64_t ok = ((uint64_t)hi << 32) | lo;
+      if (beats(ok, oe, bk, be)) {
+        bk = ok;
+        be = oe;
+      }
+    }
+    // be is the same in every lane now; its owner retires it
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (be == lane + 64 * i) avail[i] = false;
+    const double bl = tl[be];
+    if (lane == r) {
+      my_e = be;
+      my_l = bl;
+    }
+    if (r == 0) {
+      mx = bl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E) ps += exp(lv[i] - mx);
+      ps = wave_sum_d(ps);
+    }
+    psel += exp(bl - mx) / ps;
+  }
+  if (lane < k) {
+    const double p = exp(my_l - mx) / ps;
+    idx_out[lane] = my_e;
+    gate_out[lane] = (float)(renorm ? p / psel : p);
+  }
+}
 
 __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, int T, int d,
                                                const float* __restrict__ W, int E,
@@ -109,7 +183,8 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
   if (!s_last) return;
   __threadfence();
 
-  // every wave runs the same number of rounds, so the barriers are uniform
+  // one wave per token, RT_WAVES tokens per round; every wave runs the same
+  // number of rounds, so the barriers are uniform
   for (int round = 0; round < RT_TT / RT_WAVES; ++round) {
     const int tt = wave + round * RT_WAVES;
     const bool active = tt < nt;
@@ -118,52 +193,7 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
       for (int e = lane; e < E; e += 64)
         tl[wave][e] = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (!active) {
-      __syncthreads();
-      continue;
-    }
-    double lv[4];
-    int rank[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lv[i] = -INFINITY;
-      rank[i] = 0x7FFFFFFF;
-      const int e = lane + 64 * i;
-      if (e < E) {
-        lv[i] = tl[wave][e];
-        int r = 0;
-#pragma unroll 16
-        for (int o = 0; o < E; ++o) {
-          const double lo = tl[wave][o];
-          r += (lo > lv[i] || (lo == lv[i] && o < e)) ? 1 : 0;
-        }
-        rank[i] = r;
-      }
-    }
-    double mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmax(mx, lv[i]);
-    mx = wave_max_d(mx);
-    double ps = 0.0, pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = (lane + 64 * i < E) ? exp(lv[i] - mx) : 0.0;
-      ps += pv[i];
-    }
-    ps = wave_sum_d(ps);
-    double pk = 0.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (rank[i] < k) pk += pv[i] / ps;
-    const double gsum = renorm ? wave_sum_d(pk) : 1.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (rank[i] < k) {
-        const double p = pv[i] / ps;
-        idx_out[(size_t)t * k + rank[i]] = lane + 64 * i;
-        gate_out[(size_t)t * k + rank[i]] = (float)(renorm ? p / gsum : p);
-      }
-    }
+    if (active) topk_token(tl[wave], E, k, renorm, idx_out + (size_t)t * k, gate_out + (size_t)t * k, lane);
     __syncthreads();
   }
   if (threadIdx.x == 0) counters[blockIdx.y] = 0u;
