@@ -176,17 +176,18 @@ struct FfnArgs {
   int max_rchunks, n_schunks;
   const int* slot_info;
   const uint16_t* act;   // activation fragments [chunk][K/128][4][64][8]
-  const float2* asum;    // W13: (X, V) per [chunk][K/g][16]; W2: per [chunk][K/16][16]
+  const float2* asum;    // W13: (X, V) per [chunk][K/g][16]; W2: per [chunk][16][fmax/16]
   int act_stride;        // elements per chunk
   int asum_stride;       // float2 per chunk
   uint16_t* hg;          // gate/up output fragments, [chunk][fmax/128][4][64][8]
-  float2* hsg;           // gate/up output partial sums [chunk][fmax/16][16]
+  float2* hsg;           // gate/up output partial sums [chunk][16][fmax/16]
   float* obuf;           // down output [Pt][d]
 };
 
 // Raw buffer loads (resource flags of gfx9: 32-bit data format, untyped).
 constexpr uint32_t BUF_FLAGS = 0x00020000u;
-constexpr uint32_t OOB = 0x80000000u;
+constexpr uint32_t OOB = 0x80000000u;       // lane offset that reads zero
+constexpr uint32_t OOB_STEP = 0x40000000u;  // added to every offset of a step past the end (no wrap with OOB)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)BUF_FLAGS);
@@ -267,19 +268,27 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
 // ---------------------------------------------------------------------------
 // Streaming core.
 //
-// One wave = one work item: a chunk and two 16-row tiles that share the
-// chunk's activations (gate/up: gate tile u and up tile u; down: tiles 2u
-// and 2u+1).  The wave walks the k-blocks of both tiles together: per
-// k-block one plane word per lane, plane and tile, one scale per lane and
-// tile and 4 x 16 B of activation fragment per lane, prefetched PF k-blocks
-// ahead in a register ring.
+// One wave = one work item: a chunk and NT 16-row tiles that share the
+// chunk's activations (gate/up: the gate and up tiles of NT/2 row blocks;
+// down: NT consecutive tiles).  The wave walks the k-blocks of its tiles
+// together: per k-block one plane word per lane, plane and tile, a scale and
+// a zero per lane and tile, the token's group sums and 4 x 16 B of
+// activation fragment per lane, prefetched PF k-blocks ahead in a register
+// ring.  The group-sum terms are applied with the scales already in
+// registers (gate/up: every 4/QPK k-blocks; down: per k-block).
 
 constexpr int FFN_THREADS = 256;
 #ifndef FFN_WPE
 #define FFN_WPE 2  // waves per SIMD the kernel is compiled for
 #endif
 #ifndef FFN_PF
-#define FFN_PF 2   // k-blocks in flight ahead of the one being computed
+#define FFN_PF 2   // k-blocks in flight ahead of the one being computed (two-tile steps)
+#endif
+#ifndef FFN_W13_NT
+#define FFN_W13_NT 2  // gate/up tiles per step (gate and up tiles of FFN_W13_NT/2 row blocks)
+#endif
+#ifndef FFN_W2_NT
+#define FFN_W2_NT 2   // down tiles per step
 #endif
 
 template <int MODE, int QPK, int MASK>
@@ -288,7 +297,10 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   constexpr Units U = make_units(MASK);
   constexpr Classes CL = make_classes(MASK);
   constexpr int BM = mask_bmax(MASK);
-  constexpr int PF = (QPK == 2) ? 1 : FFN_PF;
+  constexpr int NT = (MODE == MODE_W13) ? FFN_W13_NT : FFN_W2_NT;  // tiles per step
+  constexpr int NP = NT / 2;                                       // gate/up: tile pairs
+  constexpr int PF = (QPK == 2 || CL.n >= 4 || NT > 2) ? 1 : FFN_PF;  // fewer slots where registers are short
+  static_assert(NT % 2 == 0, "tiles per step");
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // token row of the activation operand; weight row of D
   const int jg = lane >> 4;   // k-chunk of the operands; token quad of D
@@ -297,8 +309,13 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   const int NKB = K >> 7;
   const int NQG = K / a.g;
   const uint32_t plane_bytes = (uint32_t)((size_t)M.N * K / 8);
-  const int tile0 = (MODE == MODE_W13) ? item : 2 * item;
-  const int tile1 = (MODE == MODE_W13) ? (M.N >> 5) + item : 2 * item + 1;
+
+  // tiles of the item: gate/up -> gate tiles item*NP + p, then the matching
+  // up tiles; down -> tiles item*NT + t
+  int tile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    tile[t] = (MODE == MODE_W13) ? (t < NP ? item * NP + t : (M.N >> 5) + item * NP + (t - NP)) : item * NT + t;
 
   // token of the activation row (correction operand)
   float FA = 0.f, ctA = 0.f;
@@ -328,75 +345,74 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)c * a.act_stride, (uint32_t)K * 32);
-  const int nsum = (MODE == MODE_W13) ? NQG : (K >> 4);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)c * a.asum_stride, (uint32_t)nsum * 128);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)c * a.asum_stride, (uint32_t)a.asum_stride * 8);
+
+  // Per-lane offsets.  Group sums: gate/up reads (X, V) of one group of token
+  // r16 in the lanes of that group's k-slot; down reads two of the 16-column
+  // partial sums of token r16 per lane (group kb*QPK + (jg & (QPK - 1))).
+  // activation rows past the chunk's pairs are zero: their lanes read nothing
+  const uint32_t vo_act = r16 < m ? lane * 16 : OOB;
+  const uint32_t vo_pl = lane * 4;
+  const uint32_t vo_s = r16 * 4;
+  // Gate/up collects the group terms of SPB = 4/QPK k-blocks in the four
+  // k-slots of one correction product: k-block j puts its QPK groups in
+  // slots (j mod SPB)*QPK + h, i.e. in the lanes jg of that slot.
+  constexpr int SPB = 4 / QPK;
+  uint32_t vo_x;
+  if (MODE == MODE_W13) {
+    vo_x = (uint32_t)((jg % QPK) * 16 + r16) * 8;
+  } else {
+    const int pidx = (QPK == 1) ? 2 * jg : 4 * (jg & 1) + 2 * (jg >> 1);
+    vo_x = (uint32_t)(r16 * (a.fmax >> 4) + pidx) * 8;
+  }
 
   struct Ops {
     u32x4_t act[4];
-    uint32_t w0[BM], w1[BM];
-    float s0[QPK], s1[QPK];
+    uint32_t w[NT][BM];
+    float s[NT][QPK], z[NT][QPK];
+    u32x4_t xs;  // gate/up: (X, V) in .x, .y; down: two (X, V) partials
   };
-  const uint32_t t0off = (uint32_t)tile0 * (K / 2) * 4;
-  const uint32_t t1off = (uint32_t)tile1 * (K / 2) * 4;
-  const uint32_t s0off = (uint32_t)tile0 * NQG * 128;
-  const uint32_t s1off = (uint32_t)tile1 * NQG * 128;
-  auto load = [&](int kb, Ops& o) {
+  uint32_t toff[NT], soff[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.act[i] = bld128(ra, lane * 16 + i * 1024, kb * 4096);
+  for (int t = 0; t < NT; ++t) {
+    toff[t] = (uint32_t)tile[t] * (K / 2) * 4;
+    soff[t] = (uint32_t)tile[t] * NQG * 128;
+  }
+  // Loads of stream step j; past the end every offset is out of range (the
+  // loads return zeros and touch no memory), so each step issues the same
+  // loads and the wait counts stay exact.
+  const int NJ = NKB;
+  auto load = [&](int j, Ops& o) {
+    const uint32_t oob = (j < NJ) ? 0u : OOB_STEP;
+    const uint32_t va = vo_act + oob, vp = vo_pl + oob, vs = vo_s + oob, vx = vo_x + oob;
 #pragma unroll
-    for (int p = 0; p < BM; ++p) o.w0[p] = bld32(rp, lane * 4, t0off + kb * 256 + p * plane_bytes);
+    for (int i = 0; i < 4; ++i) o.act[i] = bld128(ra, va + i * 1024, j * 4096);
 #pragma unroll
-    for (int p = 0; p < BM; ++p) o.w1[p] = bld32(rp, lane * 4, t1off + kb * 256 + p * plane_bytes);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int h = 0; h < QPK; ++h) {
-      o.s0[h] = bldf(rs, r16 * 4, s0off + (kb * QPK + h) * 128);
-      o.s1[h] = bldf(rs, r16 * 4, s1off + (kb * QPK + h) * 128);
-    }
-  };
-
-  f32x4_t out0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, out1 = out0, corr0 = out0, corr1 = out0;
-  float cs0[QPK], cz0[QPK], cs1[QPK], cz1[QPK], cX[QPK], cV[QPK];
-
-  // correction operands of the 4*QPK groups starting at k-block kb0:
-  // lane (r16, jg) holds group kb0*QPK + 4h + jg of token / weight row r16
-  auto load_corr = [&](int kb0) {
+      for (int p = 0; p < BM; ++p) o.w[t][p] = bld32(rp, vp, toff[t] + j * 256 + p * plane_bytes);
 #pragma unroll
-    for (int h = 0; h < QPK; ++h) {
-      const int G0 = kb0 * QPK + 4 * h;
-      const bool gv = G0 + jg < NQG;
-      const uint32_t vs = gv ? (uint32_t)(jg * 32 + r16) * 4 : OOB;
-      cs0[h] = bldf(rs, vs, s0off + G0 * 128);
-      cz0[h] = bldf(rs, vs, s0off + G0 * 128 + 64);
-      cs1[h] = bldf(rs, vs, s1off + G0 * 128);
-      cz1[h] = bldf(rs, vs, s1off + G0 * 128 + 64);
-      if (MODE == MODE_W13) {
-        const float2 v = bld64f(rx, gv ? (uint32_t)(jg * 16 + r16) * 8 : OOB, G0 * 128);
-        cX[h] = v.x;
-        cV[h] = v.y;
-      } else {
-        const int tpg = a.g >> 4;  // 16-column partial sums per group
-        const uint32_t vo = gv ? (uint32_t)(jg * tpg * 16 + r16) * 8 : OOB;
-        float X = 0.f, V = 0.f;
-        for (int pt = 0; pt < tpg; ++pt) {
-          const float2 v = bld64f(rx, vo, (G0 * tpg + pt) * 128);
-          X += v.x;
-          V += v.y;
-        }
-        cX[h] = X;
-        cV[h] = V;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) {
+        o.s[t][h] = bldf(rs, vs, soff[t] + (j * QPK + h) * 128);
+        o.z[t][h] = bldf(rs, vs, soff[t] + (j * QPK + h) * 128 + 64);
       }
+    if (MODE == MODE_W13) {
+      const float2 v = bld64f(rx, (jg / QPK == j % SPB) ? vx : OOB, j * QPK * 128);
+      o.xs = u32x4_t{__float_as_uint(v.x), __float_as_uint(v.y), 0u, 0u};
+    } else {
+      o.xs = bld128(rx, vx, j * 64);
     }
   };
-  auto apply_corr = [&]() {
+
+  f32x4_t out[NT], corr[NT];
 #pragma unroll
-    for (int h = 0; h < QPK; ++h) {
-      const float Kc = ctA * cX[h] - 128.0f * FA * cV[h];
-      corr0 = mfma_f32(Kc, cs0[h], corr0);
-      corr0 = mfma_f32(cX[h], -cs0[h] * cz0[h], corr0);
-      corr1 = mfma_f32(Kc, cs1[h], corr1);
-      corr1 = mfma_f32(cX[h], -cs1[h] * cz1[h], corr1);
-    }
-  };
+  for (int t = 0; t < NT; ++t) out[t] = corr[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // gate/up: correction operands gathered over SPB k-blocks
+  float cAk = 0.f, cAx = 0.f, cBs[NT], cBz[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cBs[t] = cBz[t] = 0.f;
 
   // lanes whose k-chunk belongs to group h of a two-group k-block
   const uint32_t hmask0 = (QPK == 2 && (jg >> 1) != 0) ? 0u : 0xFFFFFFFFu;
@@ -420,7 +436,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
         for (int i = 0; i < 4; ++i) acc[k][h] = mfma_bf16(as_bf16x8(act[h][i]), as_bf16x8(W[i]), acc[k][h]);
     }
   };
-  auto tile_scale = [&](const f32x4_t (&acc)[4][QPK], const float (&s)[QPK], f32x4_t& out) {
+  auto tile_scale = [&](const f32x4_t (&acc)[4][QPK], const float (&s)[QPK], f32x4_t& o) {
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
 #pragma unroll
@@ -428,12 +444,36 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
         float v = acc[0][h][i];
 #pragma unroll
         for (int k = 1; k < CL.n; ++k) v += fac[k][i] * acc[k][h][i];
-        out[i] += s[h] * v;
+        o[i] += s[h] * v;
       }
     }
   };
+  // Group-sum terms of this k-block's groups: D += K x s - X x (s z), the
+  // k-slots of A holding parts of the group sums (down: partial sums of group
+  // kb*QPK + (jg & (QPK - 1)) in every slot), so slot jg of B carries the
+  // scale of that group.
+  auto tile_corr = [&](float Kc, float X, const float (&s)[QPK], const float (&z)[QPK], f32x4_t& cr) {
+    const float sb = (QPK == 2 && (jg & 1)) ? s[QPK - 1] : s[0];
+    const float zb = (QPK == 2 && (jg & 1)) ? z[QPK - 1] : z[0];
+    cr = mfma_f32(Kc, sb, cr);
+    cr = mfma_f32(X, -sb * zb, cr);
+  };
 
-  auto compute = [&](const Ops& o) {
+  // Matrix-core work and the scaling that reads its results are staggered by
+  // one tile: tile t's products are scaled after tile t+1's are issued (the
+  // step's last tile after the next step's first), so no scaling waits on
+  // products issued just before it.  With three or more coverage classes
+  // each tile is scaled at once, so only one tile's accumulators are live.
+  constexpr bool STAGGER = CL.n < (NT > 2 ? 2 : 3);
+  f32x4_t accb[2][4][QPK];
+  float sprev[QPK];
+#pragma unroll
+  for (int h = 0; h < QPK; ++h) {
+    sprev[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) accb[1][k][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](const Ops& o, int j) {
     u32x4_t act[QPK][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -444,19 +484,100 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
         act[QPK - 1][i] = o.act[i] & hmask1;
       }
     }
-    f32x4_t acc0[4][QPK], acc1[4][QPK];
-    tile_mfma(act, o.w0, acc0);
-    tile_mfma(act, o.w1, acc1);
-    tile_scale(acc0, o.s0, out0);
-    tile_scale(acc1, o.s1, out1);
+    float X, V;
+    if (MODE == MODE_W13) {
+      X = __uint_as_float(o.xs[0]);
+      V = __uint_as_float(o.xs[1]);
+    } else {
+      // two of the group's 16-column partial sums per lane; the k-slot sum
+      // of the correction products adds the lanes of a group together
+      X = __uint_as_float(o.xs[0]) + __uint_as_float(o.xs[2]);
+      V = __uint_as_float(o.xs[1]) + __uint_as_float(o.xs[3]);
+    }
+    const float Kc = ctA * X - 128.0f * FA * V;
+    if (MODE == MODE_W13) {
+      // lanes of this k-block's slots take its group terms (the others read zero)
+      const bool sel = (jg / QPK) == (j % SPB);
+      const int h = jg % QPK;
+      cAk += Kc;
+      cAx += X;
+      if (sel) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          cBs[t] = o.s[t][QPK == 2 ? h : 0];
+          cBz[t] = -cBs[t] * o.z[t][QPK == 2 ? h : 0];
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (STAGGER) {
+        tile_mfma(act, o.w[t], accb[t & 1]);
+        // the previous tile: this step's t-1, or the last tile of the previous step
+        if (t == 0) {
+          tile_scale(accb[1], sprev, out[NT - 1]);
+        } else {
+          tile_scale(accb[(t - 1) & 1], o.s[t - 1], out[t - 1]);
+        }
+      } else {
+        tile_mfma(act, o.w[t], accb[0]);
+        tile_scale(accb[0], o.s[t], out[t]);
+      }
+    }
+    if (STAGGER) {
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) sprev[h] = o.s[NT - 1][h];
+    }
+    if (MODE == MODE_W13) {
+      if (j % SPB == SPB - 1 || j == NJ - 1) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          corr[t] = mfma_f32(cAk, cBs[t], corr[t]);
+          corr[t] = mfma_f32(cAx, cBz[t], corr[t]);
+        }
+        cAk = cAx = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tile_corr(Kc, X, o.s[t], o.z[t], corr[t]);
+    }
   };
 
-  auto finish = [&]() {
-    const f32x4_t res0 = out0 + corr0;
-    const f32x4_t res1 = out1 + corr1;
-    if (MODE == MODE_W13) {
+  // Stream: a main loop of PF+1 unrolled steps (every step issues the loads
+  // PF steps ahead into the slot the previous step freed), then the last
+  // NJ mod (PF+1) steps, which issue nothing.  The scheduling barriers keep
+  // each step's loads together and in step order: loads retire in issue
+  // order, so a step's wait then covers its own operands and nothing issued
+  // after them.
+  Ops o[PF + 1];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    load(q, o[q]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int j0 = 0;
+  for (; j0 + PF + 1 <= NJ; j0 += PF + 1) {
+#pragma unroll
+    for (int q = 0; q <= PF; ++q) {
+      load(j0 + q + PF, o[(q + PF) % (PF + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(o[q], j0 + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (j0 + q < NJ) compute(o[q], j0 + q);
+  if (STAGGER) tile_scale(accb[1], sprev, out[NT - 1]);
+
+  if (MODE == MODE_W13) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const f32x4_t res0 = out[p] + corr[p];
+      const f32x4_t res1 = out[NP + p] + corr[NP + p];
       // h column n of the down projection's input; tokens 4jg+i
-      const int n = item * 16 + r16;
+      const int u = item * NP + p;
+      const int n = u * 16 + r16;
       const int cc = n & 31;
       const int fp = frag_pos(cc);
       const float ainv = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
@@ -480,52 +601,38 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
           Vp[i] += __shfl_xor(Vp[i], msk, WAVE);
         }
       if (r16 == 0) {
-        float4* hs = reinterpret_cast<float4*>(a.hsg + (size_t)c * (a.fmax >> 4) * 16 + item * 16 + 4 * jg);
-        hs[0] = make_float4(Xp[0], Vp[0], Xp[1], Vp[1]);
-        hs[1] = make_float4(Xp[2], Vp[2], Xp[3], Vp[3]);
-      }
-    } else {
+        float2* hs = a.hsg + (size_t)c * a.fmax + u;  // [chunk][token][fmax/16]
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = 4 * jg + i;
-        if (tk < m) {
-          float* orow = a.obuf + (size_t)(s0 + tk) * a.d;
-          orow[tile0 * 16 + r16] = res0[i];
-          orow[tile1 * 16 + r16] = res1[i];
-        }
+        for (int i = 0; i < 4; ++i) hs[(size_t)(4 * jg + i) * (a.fmax >> 4)] = make_float2(Xp[i], Vp[i]);
       }
     }
-  };
-
-  // k-block step: loads PF ahead into the slot the previous step freed,
-  // corrections every fourth k-block and at the end.
-  auto step = [&](int kb, const Ops& cur, Ops& ahead) {
-    if (kb + PF < NKB) load(kb + PF, ahead);
-    if ((kb & 3) == 0) load_corr(kb);
-    compute(cur);
-    if ((kb & 3) == 3 || kb == NKB - 1) apply_corr();
-  };
-
-  Ops o[PF + 1];
+  } else {
 #pragma unroll
-  for (int q = 0; q < PF; ++q)
-    if (q < NKB) load(q, o[q]);
-  for (int kb0 = 0; kb0 < NKB; kb0 += PF + 1) {
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 4 * jg + i;
+      if (tk < m) {
+        float* orow = a.obuf + (size_t)(s0 + tk) * a.d;
 #pragma unroll
-    for (int q = 0; q <= PF; ++q)
-      if (kb0 + q < NKB) step(kb0 + q, o[q], o[(q + PF) % (PF + 1)]);
+        for (int t = 0; t < NT; ++t) orow[tile[t] * 16 + r16] = out[t][i] + corr[t][i];
+      }
+    }
   }
-  finish();
 }
 
 template <int MODE, int QPK>
 __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN_WPE, FFN_WPE))) void k_ffn(FfnArgs a) {
-  const int gw = uniform((int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6));
-  const int nw = (int)((gridDim.x * blockDim.x) >> 6);
+  // Blocks are dealt to the 8 XCDs round-robin (block b on XCD b mod 8);
+  // each XCD walks one contiguous eighth of the item list, so a chunk's
+  // activations are fetched into at most two XCDs' L2.  (The mapping only
+  // affects where work runs, not what it computes.)
+  const int xcd = blockIdx.x & 7;
+  const int lw = uniform((int)(((blockIdx.x >> 3) * blockDim.x + threadIdx.x) >> 6));
+  const int nlw = (int)(((gridDim.x >> 3) * blockDim.x) >> 6);
   const int n_rc = a.meta[0];
   const int items_r = n_rc * a.items[0];
   const int items = items_r + a.n_schunks * a.items[1];
-  for (int w = gw; w < items; w += nw) {
+  const int w_end = (int)(((long)items * (xcd + 1)) >> 3);
+  for (int w = (int)(((long)items * xcd) >> 3) + lw; w < w_end; w += nlw) {
     int c, item, sh;
     if (w < items_r) {
       c = w / a.items[0];
@@ -600,15 +707,15 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
   FfnArgs a = make_args(s, L, ws, routed, shared);
   // work items per chunk: gate/up -> f/16 tile pairs, down -> d/32 tile pairs
   if (mode == MODE_W13) {
-    a.items[0] = s.f / 16;
-    a.items[1] = s.n_shared ? s.fs / 16 : 1;
+    a.items[0] = s.f / (8 * FFN_W13_NT);
+    a.items[1] = s.n_shared ? s.fs / (8 * FFN_W13_NT) : 1;
     a.act = reinterpret_cast<const uint16_t*>(ws + L.xg);
     a.act_stride = s.d * 16;
     a.asum = reinterpret_cast<const float2*>(ws + L.xvg);
     a.asum_stride = (s.d / s.g) * 16;
   } else {
-    a.items[0] = s.d / 32;
-    a.items[1] = s.d / 32;
+    a.items[0] = s.d / (16 * FFN_W2_NT);
+    a.items[1] = s.d / (16 * FFN_W2_NT);
     a.act = reinterpret_cast<const uint16_t*>(ws + L.hg);
     a.act_stride = s.fmax * 16;
     a.asum = reinterpret_cast<const float2*>(ws + L.hsg);
@@ -619,7 +726,7 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
   long grid = (max_items + 3) / 4;
   const long cap = (long)num_cu * FFN_WPE;  // FFN_WPE waves per SIMD x 4 SIMDs / 4 waves per block
   if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
+  grid = (grid + 7) & ~7L;  // whole rounds over the 8 XCDs
   if (mode == MODE_W13) {
     if (qpk == 2)
       hipLaunchKernelGGL((k_ffn<MODE_W13, 2>), dim3(grid), dim3(FFN_THREADS), 0, stream, a);

@@ -17,12 +17,12 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_TT = 8;  // tokens per block
+constexpr int RT_TT = 4;  // tokens per block (one wave each for top-k)
 constexpr int RT_ET = 8;  // experts per block
 constexpr int RT_WAVES = 4;
 
-template <int M>
-__device__ __forceinline__ void butterfly_step(double (&v)[64], int lane) {
+template <int M, int N>
+__device__ __forceinline__ void butterfly_step(double (&v)[N], int lane) {
   const bool up = (lane & M) != 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
@@ -30,13 +30,17 @@ __device__ __forceinline__ void butterfly_step(double (&v)[64], int lane) {
     const double keep = up ? v[i + M] : v[i];
     v[i] = keep + __shfl_xor(send, M, WAVE);
   }
-  if constexpr (M > 1) butterfly_step<M / 2>(v, lane);
+  if constexpr (M > 1) butterfly_step<M / 2, N>(v, lane);
 }
 
-// Reduce-scatter: after the step with mask M, v[0 .. M-1] hold partial sums
-// of the indices selected by the lane's higher bits; finally v[0] is the
-// wave total of index `lane`.
-__device__ __forceinline__ void butterfly64(double (&v)[64], int lane) { butterfly_step<32>(v, lane); }
+// Reduce-scatter of N = 32 values per lane: after the step with mask M,
+// v[0 .. M-1] hold partial sums of the indices selected by the lane's bits
+// below 32; the xor-32 step then folds the wave halves, so v[0] is the wave
+// total of index lane % 32.
+__device__ __forceinline__ void butterfly32(double (&v)[32], int lane) {
+  butterfly_step<16, 32>(v, lane);
+  v[0] += __shfl_xor(v[0], 32, WAVE);
+}
 
 // Order-preserving map of a double to an unsigned 64-bit key (larger logit,
 // larger key; -0 and +0 equal).  Logits are finite.
@@ -130,10 +134,11 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
   const int c_beg = wave * slice;
   const int c_end = min(d, c_beg + slice);
 
-  double acc[64];
+  double acc[RT_ET * RT_TT];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.0;
+  for (int i = 0; i < RT_ET * RT_TT; ++i) acc[i] = 0.0;
 
+#pragma unroll 2
   for (int c = c_beg + lane * 4; c < c_end; c += 256) {
     float4 wv[RT_ET];
 #pragma unroll
@@ -159,10 +164,11 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
       }
     }
   }
-  butterfly64(acc, lane);
+  static_assert(RT_ET * RT_TT == 32, "reduce-scatter width");
+  butterfly32(acc, lane);
   part[wave][lane] = acc[0];
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0 && lane < 32) {
     const int ee = lane / RT_TT, tt = lane % RT_TT;
     const int e = e0 + ee, t = t0 + tt;
     if (e < E && tt < nt) {
