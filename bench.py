@@ -11,15 +11,19 @@ expert bank (1.36 GB) are rotated and eight activation batches cycled so the
 
 The headline step runs T=32 tokens at target 3.0 bits, replayed from HIP
 graphs; a sweep over T in {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
-The roofline object is for the FFN stage (moe_anyprec_ffn: permutation,
-activation prep, gate/up + SwiGLU, down, combine), timed with HIP events on
-its stream around each call, against the algorithmic bytes of that call.
+The roofline object is for the FFN stage (moe_anyprec_ffn: plan, activation
+gather, gate/up + SwiGLU, down, combine), timed with HIP events on its
+stream around each call, against the algorithmic bytes of that call.  Its
+"traffic" is the counter-measured HBM bytes per call recorded under
+profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy), used only
+while the kernel sources still hash to the value recorded there.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -54,6 +58,34 @@ def algorithmic_ffn_bytes(idx, bits, cfg, accumulate=False):
     T = idx.size // cfg.k
     io = T * d * 2 + T * d * 4 * (2 if accumulate else 1) + idx.size * f * 2 * 2
     return planes + sz + io, float(np.mean(be[act])), float(np.mean(bits)), int(np.sum(act))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_qwen_T32_b3.0_hbm_bytes.md")
+FFN_SOURCES = ("ffn.hip", "permute.hip", "common.hpp", "kernels.hpp")
+
+
+def ffn_source_hash():
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(os.path.join(ROOT, "dynamic_any_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(T, target):
+    """Counter-measured bytes per FFN call for the T=32, 3.0-bit decode
+    workload, or None when that record is missing or older than the kernels."""
+    if T != 32 or target != 3.0 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != ffn_source_hash() or "traffic_bytes_per_launch" not in rec:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def router_bytes(cfg, T):
@@ -280,8 +312,8 @@ def main():
         "n_active_experts": ev["n_active"],
         "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "moe_anyprec_ffn (permute, xprep, w13+SwiGLU, w2, combine)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(T, args.target),
+                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
                      "bytes_per_launch": ev["ffn_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
