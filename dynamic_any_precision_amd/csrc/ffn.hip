@@ -1,33 +1,3 @@
-// Any-precision expert FFN: gate/up projection with SwiGLU, down projection,
-// gate-weighted combine.
-//
-// Math (per pair (t, e) at b planes, quant group G of row n, delta = B - b):
-//   w = ((q >> delta) * 2^delta + c_delta - z) * s,  c_delta = (2^delta - 1)/2
-// (floor-and-compensation read, MatMoE review, Core Contribution).  With
-// X_G = sum_{c in G} x_c:
-//   sum_c w x_c = s * [ sum_c ((q >> delta) << delta)(c) x_c + (c_delta - z) X_G ].
-// The kept high bits are the first b planes, (q >> delta) << delta =
-// sum_{p<b} bit_p 2^(B-1-p), so the first sum splits into plane units of one
-// or two planes; a unit (p, p+1) contributes 2^(B-2-p) * sum_c f_c x_c with
-// f = 2 bit_p + bit_{p+1} (a single plane p uses f = 2 bit_p).
-//
-// Each unit runs on the bf16 matrix cores: 16 rows x 32 columns of a unit
-// become an exact bf16 A operand (values 2^(B-2-p) (128 + f 4^a), see
-// common.hpp), the activations, pre-scaled by 4^-a and masked to the pairs
-// that read that unit, are the B operand, and v_mfma_f32_16x16x32_bf16 sums
-// them in fp32.  Per quant group the fp32 partial is multiplied by s; the
-// remaining terms s * (c_delta X_G - 128 F_t V_G) - s z X_G (V_G the
-// 4^-a-weighted group sum, F_t the sum of the unit factors the pair reads)
-// are two small fp32 products over groups, done with v_mfma_f32_16x16x4f32.
-//
-// Work items, one per 256-thread block: (chunk of <= 16 pairs of one expert,
-// row block).  W13: gate rows 32i..32i+31 and the matching up rows; W2:
-// rows 64i..64i+63.  Each wave streams one 16-row tile of the chunk's planes
-// once, in 128-bit loads from the lane-interleaved layout, and serves all
-// pairs of the chunk; a pair only receives the units its own width covers.
-#include "common.hpp"
-#include "kernels.hpp"
-
 // Any-precision expert FFN: activation gather, gate/up projection with
 // SwiGLU, down projection, gate-weighted combine.
 //

@@ -1,15 +1,14 @@
-// Router: fp64-accumulated logits GEMV, softmax over all experts and top-k,
-// in one launch.  ("routing each token to a small set of experts",
-// DPA-MoE abstract; "routing scores", MatMoE abstract.)
+// Router: fp64-accumulated logits GEMV, then softmax over all experts and
+// top-k.  ("routing each token to a small set of experts", DPA-MoE abstract;
+// "routing scores", MatMoE abstract.)
 //
-// Grid (E/8 expert tiles, T/8 token tiles), 256 threads.  The four waves of a
-// block split the hidden dimension; each accumulates the 8 x 8 (expert,
-// token) dot products of its slice in float64 from exact bf16 / fp32
-// inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
-// pair l, and wave 0 adds the four slices in a fixed order.  The last block
-// of a token tile to finish (atomic counter, reset afterwards) runs softmax
-// and top-k for the tile's tokens, one wave per token: k rounds of a
-// wave-wide arg-max over (logit desc, index asc).
+// Logits: grid (E/8 expert tiles, T/4 token tiles), 256 threads.  The four
+// waves of a block split the hidden dimension; each accumulates the 8 x 4
+// (expert, token) dot products of its slice in float64 from exact bf16 /
+// fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
+// pair l, and wave 0 adds the four slices in a fixed order.
+// Top-k: one wave per token, k rounds of a wave-wide arg-max over (logit
+// desc, index asc) through DPP lane moves.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -54,10 +53,28 @@ __device__ __forceinline__ bool beats(uint64_t ka, int ia, uint64_t kb, int ib) 
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// One step of the wave arg-max: each lane takes the better of its own
+// candidate and the candidate DPP control CTRL moves to it (lanes with no
+// source keep their own).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(uint32_t& hi, uint32_t& lo, int& ix) {
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
+  const int oix = __builtin_amdgcn_update_dpp(ix, ix, CTRL, ROWS, 0xF, false);
+  const uint64_t ok = ((uint64_t)ohi << 32) | olo, mk = ((uint64_t)hi << 32) | lo;
+  if (beats(ok, oix, mk, ix)) {
+    hi = ohi;
+    lo = olo;
+    ix = oix;
+  }
+}
+
 // Softmax over the E logits of one token and its top k, by one wave: k
-// rounds of a wave-wide arg-max over (logit desc, index asc); lane l owns
-// experts l, l+64, l+128, l+192.
-__device__ void topk_token(const double* __restrict__ tl, int E, int k, int renorm, int* __restrict__ idx_out,
+// rounds of a wave-wide arg-max; lane l owns experts l, l+64, l+128, l+192.
+// The arg-max shifts candidates right by 1, 2, 4, 8 lanes within each row of
+// 16 and then carries rows 0 and 2 into rows 1 and 3 (row broadcast 15) and
+// row 1 into rows 2 and 3 (row broadcast 31): lane 63 ends with the winner.
+__device__ void topk_token(const double* __restrict__ lg, int E, int k, int renorm, int* __restrict__ idx_out,
                            float* __restrict__ gate_out, int lane) {
   double lv[4];
   uint64_t key[4];
@@ -66,7 +83,7 @@ __device__ void topk_token(const double* __restrict__ tl, int E, int k, int reno
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     avail[i] = e < E;
-    lv[i] = avail[i] ? tl[e] : 0.0;
+    lv[i] = avail[i] ? lg[e] : 0.0;
     key[i] = avail[i] ? order_key64(lv[i]) : 0ull;
   }
   double mx = 0.0, ps = 0.0, psel = 0.0;
@@ -81,22 +98,19 @@ __device__ void topk_token(const double* __restrict__ tl, int E, int k, int reno
         bk = key[i];
         be = lane + 64 * i;
       }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)bk, m, WAVE);
-      const uint32_t hi = __shfl_xor((uint32_t)(bk >> 32), m, WAVE);
-      const int oe = __shfl_xor(be, m, WAVE);
-      const uint64_t ok = ((uint64_t)hi << 32) | lo;
-      if (beats(ok, oe, bk, be)) {
-        bk = ok;
-        be = oe;
-      }
-    }
-    // be is the same in every lane now; its owner retires it
+    uint32_t hi = (uint32_t)(bk >> 32), lo = (uint32_t)bk;
+    argmax_step<0x111, 0xF>(hi, lo, be);  // row_shr:1
+    argmax_step<0x112, 0xF>(hi, lo, be);  // row_shr:2
+    argmax_step<0x114, 0xF>(hi, lo, be);  // row_shr:4
+    argmax_step<0x118, 0xF>(hi, lo, be);  // row_shr:8
+    argmax_step<0x142, 0xA>(hi, lo, be);  // row_bcast:15
+    argmax_step<0x143, 0xC>(hi, lo, be);  // row_bcast:31
+    be = __builtin_amdgcn_readlane(be, 63);
+    // the owner retires the winner
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (be == lane + 64 * i) avail[i] = false;
-    const double bl = tl[be];
+    const double bl = lg[be];
     if (lane == r) {
       my_e = be;
       my_l = bl;
@@ -117,14 +131,19 @@ __device__ void topk_token(const double* __restrict__ tl, int E, int k, int reno
   }
 }
 
-__global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, int T, int d,
-                                               const float* __restrict__ W, int E,
-                                               const float* __restrict__ bias, int k, int renorm,
-                                               int* __restrict__ idx_out, float* __restrict__ gate_out,
-                                               double* __restrict__ logits, unsigned* __restrict__ counters) {
+// One wave per token.
+__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int k, int renorm,
+                                                    int* __restrict__ idx_out, float* __restrict__ gate_out) {
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  if (t >= T) return;
+  topk_token(logits + (size_t)t * E, E, k, renorm, idx_out + (size_t)t * k, gate_out + (size_t)t * k,
+             threadIdx.x & 63);
+}
+
+__global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ x, int T, int d,
+                                                      const float* __restrict__ W, int E,
+                                                      const float* __restrict__ bias, double* __restrict__ logits) {
   __shared__ double part[RT_WAVES][64];
-  __shared__ double tl[RT_WAVES][256];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.y * RT_TT;
@@ -178,49 +197,20 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, i
     }
   }
 
-  // ---- last block of this token tile: softmax + top-k ----
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&counters[blockIdx.y], 1u);
-    s_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // one wave per token, RT_WAVES tokens per round; every wave runs the same
-  // number of rounds, so the barriers are uniform
-  for (int round = 0; round < RT_TT / RT_WAVES; ++round) {
-    const int tt = wave + round * RT_WAVES;
-    const bool active = tt < nt;
-    const int t = t0 + (active ? tt : 0);
-    if (active)
-      for (int e = lane; e < E; e += 64)
-        tl[wave][e] = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (active) topk_token(tl[wave], E, k, renorm, idx_out + (size_t)t * k, gate_out + (size_t)t * k, lane);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) counters[blockIdx.y] = 0u;
 }
 
 }  // namespace
 
 size_t route_workspace_bytes(int T, int E) {
-  const size_t nt = (size_t)(T + RT_TT - 1) / RT_TT;
-  const size_t logits = ((size_t)T * E * sizeof(double) + 255) & ~size_t(255);
-  return logits + ((nt * sizeof(unsigned) + 255) & ~size_t(255));
+  return ((size_t)T * E * sizeof(double) + 255) & ~size_t(255);
 }
 
 hipError_t launch_route(const uint16_t* x, int T, int d, const float* W, int E, const float* bias, int k,
                         int renorm, int* idx, float* gate, void* ws, hipStream_t stream) {
-  const size_t logits_bytes = ((size_t)T * E * sizeof(double) + 255) & ~size_t(255);
   double* logits = static_cast<double*>(ws);
-  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + logits_bytes);
   dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
-  hipLaunchKernelGGL(k_route, grid, dim3(256), 0, stream, x, T, d, W, E, bias, k, renorm, idx, gate, logits,
-                     counters);
+  hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
+  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, renorm, idx, gate);
   return hipGetLastError();
 }
 
