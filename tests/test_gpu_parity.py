@@ -333,6 +333,43 @@ def test_ffn_deepseek_shared(b_lo):
     assert err < REL_L2, err
 
 
+def test_ffn_qwen_prefill_sampled_tokens():
+    # 4096 tokens with Zipf-skewed expert load: experts hold hundreds to
+    # thousands of pairs, many chunks per expert, widths mixed inside chunks
+    note("ffn cfg4 T=4096")
+    err, b = _ffn_case(4, tokens=[0, 1, 1000, 2047, 3333, 4095])
+    assert set(np.unique(b)) <= {2, 4}
+    assert err < REL_L2, err
+
+
+def test_stack_layers_teacher_forced():
+    # three layers of the 48-layer stack shape, T=64: the residual is carried
+    # on the GPU (fp32 h, bf16 layer input); each layer's output is checked
+    # against the oracle on the GPU's own layer input (teacher forcing)
+    cfg = wl.config(5)
+    rng = np.random.default_rng(5)
+    h = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)).cuda()
+    x = bd.residual_to_bf16(h)
+    rows = [0, 17, 63]
+    for layer in range(3):
+        w_router, bank = wl.make_stack_layer(cfg, layer)
+        dev_bank = bd.DeviceBank.from_host(bank)
+        note(f"stack layer {layer}")
+        idx, gate = bd.route(x, torch.from_numpy(w_router).cuda(), None, cfg.k)
+        bits = bd.alloc_bits(gate.reshape(-1), cfg.b_lo, 4, 2.0 + 0.5 * layer)
+        x_np = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        y0 = h.clone()
+        h = bd.anyprec_ffn(dev_bank, None, x, idx, gate, bits, y=h, accumulate=True)
+        torch.cuda.synchronize()
+        oc = orc.bank_cache(bank)
+        ref = orc.combine(x_np, idx.cpu().numpy(), gate.cpu().numpy().astype(np.float64),
+                          bits.cpu().numpy(), oc, tokens=rows)
+        got = h.cpu().numpy().astype(np.float64)[rows] - y0.cpu().numpy().astype(np.float64)[rows]
+        assert rel_l2(got, ref[rows]) < REL_L2, layer
+        x = bd.residual_to_bf16(h)
+        del dev_bank
+
+
 def test_ffn_drops_invalid_pairs():
     # an out-of-range expert index contributes nothing and breaks nothing
     w, dev, oc, _ = workload(1)
