@@ -47,8 +47,13 @@ FfnShape make_shape(int T, int k, int E, int B, int g, int d, int f, int n_share
   s.P = T * k;
   s.Pt = s.P + n_shared * T;
   s.W = (T + 31) / 32;
-  s.max_rchunks = (E < s.P ? E : s.P) + s.P / 16 + 1;
-  s.n_schunks = n_shared * ((T + 15) / 16);
+  // Wide chunks (64 pairs, four 16-token blocks) once experts average 32
+  // or more pairs: a workgroup then expands each weight unit once for 64
+  // tokens (the grouped matrix-core path of prefill-sized batches).
+  s.cs = (s.P >= 32 * E && f % 64 == 0 && s.fs % 64 == 0) ? 64 : 16;
+  s.sub = s.cs / 16;
+  s.max_rchunks = (E < s.P ? E : s.P) + s.P / s.cs + 1;
+  s.n_schunks = n_shared * ((T + s.cs - 1) / s.cs);
   s.fmax = s.fs > f ? s.fs : f;
   return s;
 }
@@ -59,6 +64,7 @@ FfnLayout make_layout(const FfnShape& s) {
   auto take = [&](size_t bytes) { size_t r = o; o += al256(bytes); return r; };
   const size_t NK = (size_t)s.E * s.B;
   const size_t NC = (size_t)s.max_rchunks + s.n_schunks;
+  const size_t NB = NC * s.sub;  // 16-token blocks
   L.pair_key = take((size_t)s.P * 4);
   L.bitmap = take(NK * s.W * 4);
   L.prefix = take(NK * s.W * 4);
@@ -69,11 +75,12 @@ FfnLayout make_layout(const FfnShape& s) {
   L.meta = take(64);
   L.expert_off = take((size_t)(s.E + 1) * 4);
   L.expert_maxbits = take((size_t)s.E * 4);
-  L.xg = take(NC * s.d * 16 * 2);
-  L.xvg = take(NC * (s.d / s.g) * 16 * 8);
-  L.hg = take(NC * s.fmax * 16 * 2);
-  L.hsg = take(NC * (s.fmax / 16) * 16 * 8);
+  L.xg = take(NB * s.d * 16 * 2);
+  L.xvg = take(NB * (s.d / s.g) * 16 * 8);
+  L.hg = take(NB * s.fmax * 16 * 2);
+  L.hsg = take(NB * (s.fmax / 16) * 16 * 8);
   L.obuf = take((size_t)s.Pt * s.d * 4);
+  L.hsgg = take(s.cs == 64 ? NB * (s.fmax / s.g) * 16 * 8 : 0);
   L.total = o;
   return L;
 }
@@ -151,6 +158,8 @@ struct FfnArgs {
   int asum_stride;       // float2 per chunk
   uint16_t* hg;          // gate/up output fragments, [chunk][fmax/128][4][64][8]
   float2* hsg;           // gate/up output partial sums [chunk][16][fmax/16]
+  float2* hsgg;          // wide chunks: gate/up output group sums [block][fmax/g][16]
+  int sub;               // 16-token blocks per chunk
   float* obuf;           // down output [Pt][d]
 };
 
@@ -187,7 +196,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 struct GatherArgs {
   const uint16_t* x;
-  int d, g;
+  int d, g, sub;
   const int4* chunks;
   const int* meta;
   int max_rchunks;
@@ -197,11 +206,12 @@ struct GatherArgs {
 };
 
 __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
-  const int c = blockIdx.x;
+  const int c = blockIdx.x;  // 16-token block: chunk c / sub, block c % sub of it
   const int kb = blockIdx.y;
-  if (c < a.max_rchunks && c >= a.meta[0]) return;
-  const int4 ch = a.chunks[c];
-  const int s0 = ch.y, m = ch.z;
+  const int ck = c / a.sub;
+  if (ck < a.max_rchunks && ck >= a.meta[0]) return;
+  const int4 ch = a.chunks[ck];
+  const int s0 = ch.y + 16 * (c - ck * a.sub), m = ch.z - 16 * (c - ck * a.sub);
   const int tid = threadIdx.x, t = tid >> 4, q = tid & 15;
   __shared__ uint4 frag[256];
   uint16_t* fr = reinterpret_cast<uint16_t*>(frag);
@@ -631,6 +641,328 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide chunks (prefill-sized batches): one workgroup of 4 waves per item, an
+// item being a chunk of <= 64 pairs (four 16-token blocks) and 4 row blocks
+// (gate/up: the gate and up tile of row blocks 4i..4i+3, one per wave; down:
+// tiles 8i..8i+7, two per wave).  Per 128-column k-block the activation
+// fragments of the four token blocks (16 KiB) are copied into LDS once by
+// DMA and read by all four waves; each wave expands its tiles' plane units
+// once and feeds them to the four token blocks.  Double-buffered: the copies
+// and weight loads of k-block kb+1 run while kb is computed.
+
+constexpr int WIDE_THREADS = 256;
+
+template <int MODE, int QPK, int MASK>
+__device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, int c, int e, int s0, int m, int item,
+                                         uint4* lds) {
+  constexpr Units U = make_units(MASK);
+  constexpr Classes CL = make_classes(MASK);
+  constexpr int BM = mask_bmax(MASK);
+  constexpr int NB = 4;  // token blocks
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, jg = lane >> 4;
+  const int B = a.B;
+  const int K = M.K;
+  const int NKB = K >> 7;
+  const int NQG = K / a.g;
+  const uint32_t plane_bytes = (uint32_t)((size_t)M.N * K / 8);
+  const int tile0 = (MODE == MODE_W13) ? item * 4 + wave : item * 8 + 2 * wave;
+  const int tile1 = (MODE == MODE_W13) ? (M.N >> 5) + item * 4 + wave : item * 8 + 2 * wave + 1;
+
+  // per token block: correction weights of the A-view token r16, coverage of
+  // the D-view tokens 4jg+i
+  float FA[NB], ctA[NB];
+  int cov[NB][4];  // bit k set when D-view token 4jg+i of block b reads class k
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int ta = 16 * b + r16;
+    const int bt = ta < m ? (a.slot_info[s0 + ta] >> 24) : 0;
+    FA[b] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U.n; ++u)
+      if (bt >= U.p[u] + U.np[u]) FA[b] += ldexpf(1.0f, B - 2 - U.p[u]);
+    ctA[b] = bt > 0 ? 0.5f * (ldexpf(1.0f, B - bt) - 1.0f) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int td = 16 * b + 4 * jg + i;
+      const int bd = td < m ? (a.slot_info[s0 + td] >> 24) : 0;
+      int bits = 0;
+#pragma unroll
+      for (int k = 0; k < CL.n; ++k) bits |= (bd >= CL.w[k]) ? (1 << k) : 0;
+      cov[b][i] = bits;
+    }
+  }
+  uint32_t ubias[4];
+#pragma unroll
+  for (int u = 0; u < U.n; ++u) ubias[u] = vconst(unit_bias(B - 2 - U.p[u]));
+  const UnpackConst kc = unpack_const();
+
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(M.planes + (size_t)e * B * (plane_bytes / 4), (uint32_t)B * plane_bytes);
+  const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
+  const int nbk = (int)(a.act_stride / 2048);  // k-blocks per token block in the activation buffer
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(a.asum + (size_t)c * NB * a.asum_stride, (uint32_t)(NB * a.asum_stride * 8));
+  const uint16_t* actc = a.act + (size_t)c * NB * a.act_stride;
+
+  constexpr int SPB = 4 / QPK;
+  const uint32_t vo_pl = lane * 4, vo_s = r16 * 4;
+  // group sums (X, V) of group kb*QPK + (jg % QPK), token r16, in the lanes
+  // of the k-block's slot; one load per token block
+  const uint32_t vo_x = (uint32_t)((jg % QPK) * 16 + r16) * 8;
+  const uint32_t t0off = (uint32_t)tile0 * (K / 2) * 4, t1off = (uint32_t)tile1 * (K / 2) * 4;
+  const uint32_t s0off = (uint32_t)tile0 * NQG * 128, s1off = (uint32_t)tile1 * NQG * 128;
+
+  struct Wts {
+    uint32_t w[2][BM];
+    float s[2][QPK], z[2][QPK];
+    float2 xs[NB];
+  };
+  auto load_w = [&](int kb, Wts& o) {
+#pragma unroll
+    for (int p = 0; p < BM; ++p) {
+      o.w[0][p] = bld32(rp, vo_pl, t0off + kb * 256 + p * plane_bytes);
+      o.w[1][p] = bld32(rp, vo_pl, t1off + kb * 256 + p * plane_bytes);
+    }
+#pragma unroll
+    for (int h = 0; h < QPK; ++h) {
+      o.s[0][h] = bldf(rs, vo_s, s0off + (kb * QPK + h) * 128);
+      o.z[0][h] = bldf(rs, vo_s, s0off + (kb * QPK + h) * 128 + 64);
+      o.s[1][h] = bldf(rs, vo_s, s1off + (kb * QPK + h) * 128);
+      o.z[1][h] = bldf(rs, vo_s, s1off + (kb * QPK + h) * 128 + 64);
+    }
+    const uint32_t vx = (jg / QPK == kb % SPB) ? vo_x : OOB;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o.xs[b] = bld64f(rx, vx, (uint32_t)(b * a.asum_stride * 8 + kb * QPK * 128));
+  };
+  // activation fragments of k-block kb for the four token blocks -> LDS
+  // buffer: wave w copies token block w, 4 x 1 KiB
+  auto copy_act = [&](int kb, int buf) {
+    const uint16_t* src = actc + (size_t)wave * a.act_stride + (size_t)kb * 2048 + lane * 8;
+    uint4* dst = lds + (size_t)(buf * NB + wave) * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + i * 512), (__attribute__((address_space(3))) void*)(dst + i * 64),
+                                       16, 0, 0);
+  };
+  (void)nbk;
+
+  f32x4_t out[2][NB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) out[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float cAk[NB], cAx[NB], cBs[2], cBz[2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) cAk[b] = cAx[b] = 0.f;
+  cBs[0] = cBs[1] = cBz[0] = cBz[1] = 0.f;
+  const uint32_t hmask0 = (QPK == 2 && (jg >> 1) != 0) ? 0u : 0xFFFFFFFFu;
+  const uint32_t hmask1 = (QPK == 2 && (jg >> 1) != 1) ? 0u : 0xFFFFFFFFu;
+
+  auto compute = [&](const Wts& o, int kb, int buf) {
+    // group terms of this k-block
+    const bool sel = (jg / QPK) == (kb % SPB);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      cAk[b] += ctA[b] * o.xs[b].x - 128.0f * FA[b] * o.xs[b].y;
+      cAx[b] += o.xs[b].x;
+    }
+    if (sel) {
+      const int h = jg % QPK;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        cBs[t] = o.s[t][QPK == 2 ? h : 0];
+        cBz[t] = -cBs[t] * o.z[t][QPK == 2 ? h : 0];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4_t W[4][4];
+#pragma unroll
+      for (int u = 0; u < U.n; ++u) {
+        const uint32_t hi = o.w[t][U.p[u]];
+        const uint32_t lo = (U.np[u] == 2) ? o.w[t][U.p[u] + 1] : 0u;
+        unpack_unit(hi, lo, U.np[u] == 2, ubias[u], kc, W[u]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4* src = lds + (size_t)(buf * NB + b) * 256 + lane;
+        u32x4_t act[QPK][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t v = as_u32x4(src[i * 64]);
+          if (QPK == 1) {
+            act[0][i] = v;
+          } else {
+            act[0][i] = v & hmask0;
+            act[QPK - 1][i] = v & hmask1;
+          }
+        }
+        f32x4_t acc[4][QPK];
+#pragma unroll
+        for (int k = 0; k < CL.n; ++k)
+#pragma unroll
+          for (int h = 0; h < QPK; ++h) acc[k][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < U.n; ++u) {
+          const int k = CL.of_unit[u];
+#pragma unroll
+          for (int h = 0; h < QPK; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[k][h] = mfma_bf16(as_bf16x8(act[h][i]), as_bf16x8(W[u][i]), acc[k][h]);
+        }
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = acc[0][h][i];
+#pragma unroll
+            for (int k = 1; k < CL.n; ++k) v += ((cov[b][i] >> k) & 1) ? acc[k][h][i] : 0.f;
+            out[t][b][i] += o.s[t][h] * v;
+          }
+        }
+      }
+    }
+    if (kb % SPB == SPB - 1 || kb == NKB - 1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          out[t][b] = mfma_f32(cAk[b], cBs[t], out[t][b]);
+          out[t][b] = mfma_f32(cAx[b], cBz[t], out[t][b]);
+        }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) cAk[b] = cAx[b] = 0.f;
+    }
+  };
+
+  Wts wa, wb;
+  copy_act(0, 0);
+  load_w(0, wa);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero
+  __syncthreads();
+  for (int kb = 0; kb < NKB; kb += 2) {
+    if (kb + 1 < NKB) {
+      copy_act(kb + 1, 1);
+      load_w(kb + 1, wb);
+    }
+    compute(wa, kb, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < NKB) {
+      if (kb + 2 < NKB) {
+        copy_act(kb + 2, 0);
+        load_w(kb + 2, wa);
+      }
+      compute(wb, kb + 1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // epilogue per token block
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int bid = c * NB + b;
+    if (MODE == MODE_W13) {
+      const int u = item * 4 + wave;   // row block = 16 h columns
+      const int n = u * 16 + r16;
+      const int cc = n & 31;
+      const int fp = frag_pos(cc);
+      const float ainv = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+      uint16_t* hrow = a.hg + (size_t)bid * a.fmax * 16 +
+                       ((size_t)((n >> 7) * 4 + (fp >> 3)) * 64 + ((n & 127) >> 5) * 16) * 8 + (fp & 7);
+      float Xp[4], Vp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gval = out[0][b][i];
+        const float hval = gval / (1.0f + expf(-gval)) * out[1][b][i];
+        const float hf = bf16_to_f32(f32_to_bf16(hval));
+        hrow[(4 * jg + i) * 8] = (uint16_t)f32_to_bf16(hf * ainv);
+        Xp[i] = hf;
+        Vp[i] = hf * ainv;
+      }
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Xp[i] += __shfl_xor(Xp[i], msk, WAVE);
+          Vp[i] += __shfl_xor(Vp[i], msk, WAVE);
+        }
+      if (r16 == 0) {
+        float2* hs = a.hsg + (size_t)bid * a.fmax + u;  // [block][token][fmax/16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[(size_t)(4 * jg + i) * (a.fmax >> 4)] = make_float2(Xp[i], Vp[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = 16 * b + 4 * jg + i;
+        if (tk < m) {
+          float* orow = a.obuf + (size_t)(s0 + tk) * a.d;
+          orow[tile0 * 16 + r16] = out[0][b][i];
+          orow[tile1 * 16 + r16] = out[1][b][i];
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int QPK>
+__global__ __launch_bounds__(WIDE_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_wide(FfnArgs a) {
+  __shared__ uint4 lds[2 * 4 * 256];  // two k-blocks x four token blocks x 4 KiB
+  const int n_rc = a.meta[0];
+  const int items_r = n_rc * a.items[0];
+  const int w = blockIdx.x;
+  if (w >= items_r + a.n_schunks * a.items[1]) return;
+  int c, item, sh;
+  if (w < items_r) {
+    c = w / a.items[0];
+    item = w - c * a.items[0];
+    sh = 0;
+  } else {
+    const int w2 = w - items_r;
+    const int cs = w2 / a.items[1];
+    item = w2 - cs * a.items[1];
+    c = a.max_rchunks + cs;
+    sh = 1;
+  }
+  const int4 ch = a.chunks[c];
+  const MatrixDev& M = a.m[sh];
+  switch (ch.w & 15) {
+#define MOE_CASE(MK) \
+  case MK:           \
+    run_wide<MODE, QPK, MK>(a, M, c, ch.x, ch.y, ch.z, item, lds); \
+    break;
+    MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+    MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
+#undef MOE_CASE
+    default:
+      break;
+  }
+}
+
+// Wide chunks: group sums of the gate/up output per 16-token block, token
+// and quant group of the down projection's input, from the 16-column
+// partial sums.  One thread per (block, group, token).
+__global__ __launch_bounds__(256) void k_hsum(const FfnArgs a, int nblocks, int ngroups) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks * ngroups * 16) return;
+  const int t = i & 15, G = (i >> 4) % ngroups, bid = (i >> 4) / ngroups;
+  const int tpg = a.g >> 4;
+  const float2* src = a.hsg + (size_t)bid * a.fmax + (size_t)t * (a.fmax >> 4) + G * tpg;
+  float X = 0.f, V = 0.f;
+  for (int p = 0; p < tpg; ++p) {
+    X += src[p].x;
+    V += src[p].y;
+  }
+  a.hsgg[((size_t)bid * (a.fmax / a.g) + G) * 16 + t] = make_float2(X, V);
+}
+
 // ---------------------------------------------------------------------------
 // combine: y[t] = (acc ? y[t] : 0) + sum_j gate[t][j] o_(t,j) + sum_s o_(t,shared s)
 
@@ -669,6 +1001,8 @@ FfnArgs make_args(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev rou
   a.hg = reinterpret_cast<uint16_t*>(ws + L.hg);
   a.hsg = reinterpret_cast<float2*>(ws + L.hsg);
   a.obuf = reinterpret_cast<float*>(ws + L.obuf);
+  a.hsgg = reinterpret_cast<float2*>(ws + L.hsgg);
+  a.sub = s.sub;
   return a;
 }
 
@@ -692,6 +1026,33 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
     a.asum_stride = (s.fmax / 16) * 16;
   }
   const int qpk = (s.g == 64) ? 2 : 1;
+  if (s.cs == 64) {
+    // wide chunks: 4 row blocks (gate/up) or 8 tiles (down) per workgroup
+    if (mode == MODE_W13) {
+      a.items[0] = s.f / 64;
+      a.items[1] = s.n_shared ? s.fs / 64 : 1;
+    } else {
+      a.items[0] = s.d / 128;
+      a.items[1] = s.d / 128;
+      a.asum = a.hsgg;
+      a.asum_stride = (s.fmax / s.g) * 16;
+      const int nb = (s.max_rchunks + s.n_schunks) * s.sub, ng = s.fmax / s.g;
+      hipLaunchKernelGGL(k_hsum, dim3((nb * ng * 16 + 255) / 256), dim3(256), 0, stream, a, nb, ng);
+    }
+    const long items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
+    if (mode == MODE_W13) {
+      if (qpk == 2)
+        hipLaunchKernelGGL((k_wide<MODE_W13, 2>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_wide<MODE_W13, 1>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+    } else {
+      if (qpk == 2)
+        hipLaunchKernelGGL((k_wide<MODE_W2, 2>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_wide<MODE_W2, 1>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   const long max_items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
   long grid = (max_items + 3) / 4;
   const long cap = (long)num_cu * FFN_WPE;  // FFN_WPE waves per SIMD x 4 SIMDs / 4 waves per block
@@ -718,13 +1079,14 @@ hipError_t launch_gather(const FfnShape& s, const FfnLayout& L, char* ws, const 
   a.x = x;
   a.d = s.d;
   a.g = s.g;
+  a.sub = s.sub;
   a.chunks = reinterpret_cast<const int4*>(ws + L.chunks);
   a.meta = reinterpret_cast<const int*>(ws + L.meta);
   a.max_rchunks = s.max_rchunks;
   a.slot_info = reinterpret_cast<const int*>(ws + L.slot_info);
   a.xg = reinterpret_cast<uint16_t*>(ws + L.xg);
   a.xvg = reinterpret_cast<float2*>(ws + L.xvg);
-  hipLaunchKernelGGL(k_gather, dim3(s.max_rchunks + s.n_schunks, s.d / 128), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_gather, dim3((s.max_rchunks + s.n_schunks) * s.sub, s.d / 128), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

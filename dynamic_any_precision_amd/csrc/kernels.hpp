@@ -26,11 +26,14 @@ struct FfnShape {
   int max_rchunks;       // routed chunk capacity
   int n_schunks;         // shared chunks
   int fmax;              // max(f, fs)
+  int cs;                // pairs per chunk: 16 (decode), or 64 (prefill: four 16-token blocks)
+  int sub;               // 16-token blocks per chunk (cs / 16)
 };
 
 struct FfnLayout {
   size_t pair_key, bitmap, prefix, slot_pair, pair_slot, slot_info, chunks, meta, expert_off, expert_maxbits;
   size_t xg, xvg, hg, hsg, obuf;  // chunk activation fragments and sums, gate/up output, down output
+  size_t hsgg;                    // wide chunks: group sums of the gate/up output
   size_t total;
 };
 

@@ -7,7 +7,8 @@
 //     pairs of its key is the number of earlier tokens carrying that key:
 //     one bit per (key, token) set with atomicOr, then per-key prefix
 //     popcounts.  The order is deterministic;
-//   - chunks of at most 16 consecutive pairs of one expert, each with the set
+//   - chunks of at most 16 (64 for prefill-sized batches) consecutive pairs
+//     of one expert, each with the set
 //     of bit-widths it holds (the planes it must stream are those of its
 //     widest pair, "reads the maximum bits any token of an expert needs");
 //   - chunks for the always-on shared experts.
@@ -151,14 +152,14 @@ __device__ void permute_body(const FfnShape& s, const PlanPtrs& pp, const int* _
     int m = 0, nch = 0;
     if (e < E) {
       m = off[(e + 1) * B] - off[e * B];
-      nch = (m + 15) >> 4;
+      nch = (m + s.cs - 1) / s.cs;
     }
     int total;
     const int cbase = block_exclusive_scan(nch, wsum, &total);
     if (e < E) {
       for (int c = 0; c < nch; ++c) {
-        const int s0 = off[e * B] + 16 * c;
-        const int mm = min(16, m - 16 * c);
+        const int s0 = off[e * B] + s.cs * c;
+        const int mm = min(s.cs, m - s.cs * c);
         int mask = 0;
         for (int L = 0; L < B; ++L) {
           const int lo = off[e * B + L], hi = off[e * B + L + 1];
@@ -171,11 +172,11 @@ __device__ void permute_body(const FfnShape& s, const PlanPtrs& pp, const int* _
   }
 
   // shared experts: every token, full width
-  const int ncs = (s.T + 15) >> 4;
+  const int ncs = (s.T + s.cs - 1) / s.cs;
   for (int i = tid; i < s.n_shared * ncs; i += PM_NT) {
     const int sh = i / ncs, c = i % ncs;
     pp.chunks[s.max_rchunks + i] =
-        make_int4(sh, P + sh * s.T + 16 * c, min(16, s.T - 16 * c), (1 << (B - 1)) | (1 << 16));
+        make_int4(sh, P + sh * s.T + s.cs * c, min(s.cs, s.T - s.cs * c), (1 << (B - 1)) | (1 << 16));
   }
   for (int i = tid; i < s.n_shared * s.T; i += PM_NT) pp.slot_info[P + i] = (i % s.T) | (B << 24);
 }

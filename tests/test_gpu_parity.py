@@ -242,8 +242,8 @@ def test_permute_stable_order(cfg_id):
 # expert FFN
 
 
-def _ffn_case(i, bits_np=None, tokens=None, target=None, accumulate=False, T=None, **kw):
-    w, dev, oc, sc = workload(i, **kw)
+def _ffn_case(i, bits_np=None, tokens=None, target=None, accumulate=False, T=None, over=None, **kw):
+    w, dev, oc, sc = workload(i, **kw, **(over or {}))
     cfg = w.cfg
     x = dev["x"]
     x_np = w.x_bf16
@@ -339,6 +339,40 @@ def test_ffn_qwen_prefill_sampled_tokens():
     note("ffn cfg4 T=4096")
     err, b = _ffn_case(4, tokens=[0, 1, 1000, 2047, 3333, 4095])
     assert set(np.unique(b)) <= {2, 4}
+    assert err < REL_L2, err
+
+
+# 32 or more pairs per expert on average switch the layer to chunks of 64
+# pairs (four 16-token blocks per workgroup): ragged chunk tails, empty
+# blocks, both group sizes, mixed widths and shared experts
+
+
+@pytest.mark.parametrize("g,T", [(64, 128), (64, 150), (128, 300)])
+def test_ffn_wide_chunks_full(g, T):
+    note(f"ffn cfg1 wide g={g} T={T}")
+    err, _ = _ffn_case(1, over=dict(g=g, T=T))
+    assert err < REL_L2, err
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ffn_wide_chunks_arbitrary_bit_mix(seed):
+    w, _, _, _ = workload(1, g=128, T=300)
+    rng = np.random.default_rng(10 + seed)
+    b = rng.integers(1, 5, size=w.cfg.P)
+    note(f"ffn cfg1 wide random bits seed={seed}")
+    err, _ = _ffn_case(1, bits_np=b, over=dict(g=128, T=300))
+    assert err < REL_L2, err
+
+
+def test_ffn_wide_chunks_accumulate():
+    note("ffn cfg1 wide accumulate")
+    err, _ = _ffn_case(1, accumulate=True, over=dict(g=64, T=200))
+    assert err < REL_L2, err
+
+
+def test_ffn_wide_chunks_deepseek_shared():
+    note("ffn cfg3 wide T=384")
+    err, _ = _ffn_case(3, tokens=[0, 1, 100, 383], over=dict(T=384))
     assert err < REL_L2, err
 
 
