@@ -68,6 +68,8 @@ FfnLayout make_layout(const FfnShape& s) {
   L.pair_key = take((size_t)s.P * 4);
   L.bitmap = take(NK * s.W * 4);
   L.prefix = take(NK * s.W * 4);
+  L.colerr = take((size_t)s.W * 4);
+  L.keycnt = take(NK * 4);
   L.slot_pair = take((size_t)s.P * 4);
   L.pair_slot = take((size_t)s.P * 4);
   L.slot_info = take((size_t)s.Pt * 4);

@@ -30,7 +30,8 @@
  *     launch errors.  Data-dependent contract violations (an expert index
  *     out of range, a bit-width outside [1, b_max], duplicate experts in one
  *     token's top-k) never make a kernel read or write out of bounds: such
- *     pairs are dropped from the output.
+ *     pairs are dropped from the output (of duplicates, the first pair with a
+ *     valid width is kept).
  *   - No C++ exception crosses the ABI.  The library keeps no state between
  *     calls except a cached device property, so calls are thread-safe; calls
  *     that share a workspace must be ordered on one stream.
@@ -203,7 +204,7 @@ moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank*
  * its own, for inspection.  Pairs are ordered stably by (expert ascending,
  * bits descending, pair id ascending), pair id = t*top_k + j.
  *   slot_pair       [T*top_k] int32 (output): pair id at each sorted position
- *                   (-1 where a dropped pair left a hole)
+ *                   (the kept pairs first, then -1 once per dropped pair)
  *   expert_offsets  [E+1] int32 (output): first sorted position of each expert
  *   expert_maxbits  [E] int32 (output): largest bit-width among the expert's
  *                   pairs (0 for an expert with no pair)

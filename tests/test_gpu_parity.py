@@ -238,6 +238,60 @@ def test_permute_stable_order(cfg_id):
     assert np.array_equal(emax.cpu().numpy(), mb)
 
 
+def _messy_routing(T, k, E, B, seed):
+    """Top-k lists with repeated experts, out-of-range experts and widths
+    outside [1, B] mixed in."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    bits = rng.integers(1, B + 1, size=(T, k)).astype(np.uint8)
+    u = rng.random((T, k))
+    for t, j in zip(*np.nonzero(u < 0.03)):
+        if j > 0:
+            idx[t, j] = idx[t, rng.integers(0, j)]  # repeat an earlier expert
+    idx[u > 0.99] = E + 3
+    idx[(u > 0.98) & (u <= 0.985)] = -1
+    bits[(u > 0.97) & (u <= 0.975)] = 0
+    bits[(u > 0.96) & (u <= 0.965)] = B + 1
+    return idx, bits
+
+
+def _expected_plan(idx, bits, E, B):
+    T, k = idx.shape
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e, b = int(idx[t, j]), int(bits[t, j])
+            if 0 <= e < E and 1 <= b <= B:
+                if e not in seen:
+                    keep[t, j] = True
+                seen.add(e)
+    e_f, b_f, k_f = idx.ravel().astype(np.int64), bits.ravel().astype(np.int64), keep.ravel()
+    pid = np.nonzero(k_f)[0]
+    order = pid[np.lexsort((pid, -b_f[pid], e_f[pid]))]
+    sp = np.full(T * k, -1, dtype=np.int64)
+    sp[:order.size] = order
+    counts = np.bincount(e_f[pid], minlength=E)
+    mb = np.zeros(E, dtype=np.int64)
+    np.maximum.at(mb, e_f[pid], b_f[pid])
+    return sp, np.concatenate([[0], np.cumsum(counts)]), mb
+
+
+@pytest.mark.parametrize("T,k,E", [(100, 2, 8), (37, 8, 128), (300, 6, 64), (5000, 6, 64), (20000, 8, 128)])
+def test_permute_drops_invalid_and_repeated(T, k, E):
+    # both plan variants: one block with the words in LDS (small batches) and
+    # the three-launch plan (large batches)
+    idx, bits = _messy_routing(T, k, E, 4, seed=T)
+    ws = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+    note(f"permute messy T={T} k={k} E={E}")
+    sp, eoff, emax = bd.permute(torch.from_numpy(idx).cuda(), torch.from_numpy(bits).cuda(), E, 4, ws)
+    torch.cuda.synchronize()
+    sp_ref, eoff_ref, mb_ref = _expected_plan(idx, bits, E, 4)
+    assert np.array_equal(sp.cpu().numpy(), sp_ref)
+    assert np.array_equal(eoff.cpu().numpy(), eoff_ref)
+    assert np.array_equal(emax.cpu().numpy(), mb_ref)
+
+
 # ---------------------------------------------------------------------------
 # expert FFN
 
@@ -367,6 +421,13 @@ def test_ffn_wide_chunks_arbitrary_bit_mix(seed):
 def test_ffn_wide_chunks_accumulate():
     note("ffn cfg1 wide accumulate")
     err, _ = _ffn_case(1, accumulate=True, over=dict(g=64, T=200))
+    assert err < REL_L2, err
+
+
+def test_ffn_wide_chunks_large_plan():
+    # 9000 pairs: the plan runs as three launches over the chip
+    note("ffn cfg1 wide T=4500")
+    err, _ = _ffn_case(1, tokens=list(range(0, 4500, 97)) + [4499], over=dict(g=128, T=4500))
     assert err < REL_L2, err
 
 
