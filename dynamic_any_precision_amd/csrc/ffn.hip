@@ -74,6 +74,7 @@ FfnLayout make_layout(const FfnShape& s) {
   L.pair_slot = take((size_t)s.P * 4);
   L.slot_info = take((size_t)s.Pt * 4);
   L.chunks = take(NC * 16);
+  L.chunk_cnt = take(NC * 4);
   L.meta = take(64);
   L.expert_off = take((size_t)(s.E + 1) * 4);
   L.expert_maxbits = take((size_t)s.E * 4);
@@ -151,6 +152,7 @@ struct FfnArgs {
   int items[2];          // work items per chunk (routed, shared)
   int B, g, T, P, d, fmax;
   const int4* chunks;
+  const int* chunk_cnt;  // per chunk: pairs of width >= b in byte b-1
   const int* meta;
   int max_rchunks, n_schunks;
   const int* slot_info;
@@ -189,6 +191,12 @@ __device__ __forceinline__ float2 bld64f(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Width of pair t of a chunk from its counts of pairs of width >= b (pairs
+// are sorted by width, widest first); 0 past the chunk's end.
+__device__ __forceinline__ int width_of(int cnt, int t) {
+  return (t < (cnt & 255)) + (t < ((cnt >> 8) & 255)) + (t < ((cnt >> 16) & 255)) + (t < ((cnt >> 24) & 255));
+}
 
 // ---------------------------------------------------------------------------
 // Activation gather: one block per (chunk, 128-column k-block).  Token rows
@@ -275,7 +283,7 @@ constexpr int FFN_THREADS = 256;
 
 template <int MODE, int QPK, int MASK>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, int c, int e, int s0, int m,
-                                         int item) {
+                                         int cnt, int item) {
   constexpr Units U = make_units(MASK);
   constexpr Classes CL = make_classes(MASK);
   constexpr int BM = mask_bmax(MASK);
@@ -302,7 +310,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   // token of the activation row (correction operand)
   float FA = 0.f, ctA = 0.f;
   {
-    const int bt = r16 < m ? (a.slot_info[s0 + r16] >> 24) : 0;
+    const int bt = width_of(cnt, r16);
 #pragma unroll
     for (int u = 0; u < U.n; ++u)
       if (bt >= U.p[u] + U.np[u]) FA += ldexpf(1.0f, B - 2 - U.p[u]);
@@ -312,8 +320,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   float fac[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tk = 4 * jg + i;
-    const int bt = tk < m ? (a.slot_info[s0 + tk] >> 24) : 0;
+    const int bt = width_of(cnt, 4 * jg + i);
 #pragma unroll
     for (int k = 0; k < 4; ++k) fac[k][i] = (k < CL.n && bt >= CL.w[k]) ? 1.0f : 0.0f;
   }
@@ -605,34 +612,54 @@ template <int MODE, int QPK>
 __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN_WPE, FFN_WPE))) void k_ffn(FfnArgs a) {
   // Blocks are dealt to the 8 XCDs round-robin (block b on XCD b mod 8);
   // each XCD walks one contiguous eighth of the item list, so a chunk's
-  // activations are fetched into at most two XCDs' L2.  (The mapping only
-  // affects where work runs, not what it computes.)
+  // activations are fetched into at most two XCDs' L2 and an XCD streams
+  // few experts' planes at a time.  (The mapping only affects where work
+  // runs, not what it computes.)  The next item's chunk record loads while
+  // the current item streams.
   const int xcd = blockIdx.x & 7;
   const int lw = uniform((int)(((blockIdx.x >> 3) * blockDim.x + threadIdx.x) >> 6));
   const int nlw = (int)(((gridDim.x >> 3) * blockDim.x) >> 6);
-  const int n_rc = a.meta[0];
-  const int items_r = n_rc * a.items[0];
+  const int items_r = a.meta[0] * a.items[0];
   const int items = items_r + a.n_schunks * a.items[1];
-  const int w_end = (int)(((long)items * (xcd + 1)) >> 3);
-  for (int w = (int)(((long)items * xcd) >> 3) + lw; w < w_end; w += nlw) {
+  struct Item {
     int c, item, sh;
+    u32x4_t ch;    // chunk record (every lane holds the same value)
+    uint32_t cnt;
+  };
+  const int NC = a.max_rchunks + a.n_schunks;
+  const __amdgpu_buffer_rsrc_t rch = make_rsrc(a.chunks, (uint32_t)NC * 16);
+  const __amdgpu_buffer_rsrc_t rcn = make_rsrc(a.chunk_cnt, (uint32_t)NC * 4);
+  auto fetch = [&](int w, Item& it) {
     if (w < items_r) {
-      c = w / a.items[0];
-      item = w - c * a.items[0];
-      sh = 0;
+      it.c = w / a.items[0];
+      it.item = w - it.c * a.items[0];
+      it.sh = 0;
     } else {
       const int w2 = w - items_r;
       const int cs = w2 / a.items[1];
-      item = w2 - cs * a.items[1];
-      c = a.max_rchunks + cs;
-      sh = 1;
+      it.item = w2 - cs * a.items[1];
+      it.c = a.max_rchunks + cs;
+      it.sh = 1;
     }
-    const int4 ch = a.chunks[c];
-    const MatrixDev& M = a.m[sh];
-    switch (ch.w & 15) {
+    it.ch = bld128(rch, 0u, (uint32_t)it.c * 16);
+    it.cnt = bld32(rcn, 0u, (uint32_t)it.c * 4);
+  };
+  const MatrixDev m0 = a.m[0], m1 = a.m[1];
+  const int w_end = (int)(((long)items * (xcd + 1)) >> 3);
+  int w = (int)(((long)items * xcd) >> 3) + lw;
+  if (w >= w_end) return;
+  Item it, nt;
+  fetch(w, it);
+  for (;; w += nlw) {
+    const bool more = w + nlw < w_end;
+    if (more) fetch(w + nlw, nt);
+    const MatrixDev M = it.sh ? m1 : m0;
+    const int ce = uniform((int)it.ch[0]), cs0 = uniform((int)it.ch[1]), cm = uniform((int)it.ch[2]);
+    const int cmask = uniform((int)it.ch[3]), ccnt = uniform((int)it.cnt);
+    switch (cmask & 15) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_item<MODE, QPK, MK>(a, M, c, ch.x, ch.y, ch.z, item); \
+    run_item<MODE, QPK, MK>(a, M, it.c, ce, cs0, cm, ccnt, it.item); \
     break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
       MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
@@ -640,6 +667,8 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN
       default:
         break;
     }
+    if (!more) break;
+    it = nt;
   }
 }
 
@@ -996,6 +1025,7 @@ FfnArgs make_args(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev rou
   a.m[1] = shared;
   a.B = s.B; a.g = s.g; a.T = s.T; a.P = s.P; a.d = s.d; a.fmax = s.fmax;
   a.chunks = reinterpret_cast<const int4*>(ws + L.chunks);
+  a.chunk_cnt = reinterpret_cast<const int*>(ws + L.chunk_cnt);
   a.meta = reinterpret_cast<const int*>(ws + L.meta);
   a.max_rchunks = s.max_rchunks;
   a.n_schunks = s.n_schunks;

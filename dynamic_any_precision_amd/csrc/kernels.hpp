@@ -31,8 +31,8 @@ struct FfnShape {
 };
 
 struct FfnLayout {
-  size_t pair_key, bitmap, prefix, colerr, keycnt, slot_pair, pair_slot, slot_info, chunks, meta, expert_off,
-      expert_maxbits;
+  size_t pair_key, bitmap, prefix, colerr, keycnt, slot_pair, pair_slot, slot_info, chunks, chunk_cnt, meta,
+      expert_off, expert_maxbits;
   size_t xg, xvg, hg, hsg, obuf;  // chunk activation fragments and sums, gate/up output, down output
   size_t hsgg;                    // wide chunks: group sums of the gate/up output
   size_t total;

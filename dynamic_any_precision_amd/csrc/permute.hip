@@ -13,7 +13,9 @@
 //     of an expert needs";
 //   - chunks of at most 16 (64 for prefill-sized batches) consecutive pairs
 //     of one expert, each with the set of bit-widths it holds (the planes it
-//     streams are those of its widest pair);
+//     streams are those of its widest pair) and the number of its pairs of
+//     width >= b for b = 1..4 (pairs are sorted by width, so these counts give
+//     every pair's width);
 //   - chunks for the always-on shared experts.
 // A pair is dropped (never indexed) when its expert index is out of range,
 // its width is outside [1, b_max], or an earlier pair of its token already
@@ -68,6 +70,7 @@ struct PlanPtrs {
   int* pair_slot;
   int* slot_info;
   int4* chunks;
+  int* chunk_cnt;
   int* meta;
   int* expert_off;
   int* expert_maxbits;
@@ -139,12 +142,15 @@ __device__ void plan_chunks(const FfnShape& s, const PlanPtrs& pp, const int* of
       for (int c = 0; c < nch; ++c) {
         const int s0 = off[e * B] + s.cs * c;
         const int mm = min(s.cs, m - s.cs * c);
-        int mask = 0;
+        int mask = 0, cnt = 0;
         for (int L = 0; L < B; ++L) {
           const int lo = off[e * B + L], hi = off[e * B + L + 1];
           if (hi > lo && hi > s0 && lo < s0 + mm) mask |= 1 << (B - L - 1);  // bit (b-1) for width b
+          // pairs of the chunk with width >= B - L
+          cnt |= min(max(hi - s0, 0), mm) << (8 * (B - L - 1));
         }
         pp.chunks[cbase + c] = make_int4(e, s0, mm, mask);
+        pp.chunk_cnt[cbase + c] = cnt;
       }
     }
     if (tid == 0) pp.meta[0] = total;
@@ -153,8 +159,11 @@ __device__ void plan_chunks(const FfnShape& s, const PlanPtrs& pp, const int* of
   const int ncs = (s.T + s.cs - 1) / s.cs;
   for (int i = tid; i < s.n_shared * ncs; i += PM_NT) {
     const int sh = i / ncs, c = i % ncs;
-    pp.chunks[s.max_rchunks + i] =
-        make_int4(sh, s.P + sh * s.T + s.cs * c, min(s.cs, s.T - s.cs * c), (1 << (B - 1)) | (1 << 16));
+    const int mm = min(s.cs, s.T - s.cs * c);
+    pp.chunks[s.max_rchunks + i] = make_int4(sh, s.P + sh * s.T + s.cs * c, mm, (1 << (B - 1)) | (1 << 16));
+    int cnt = 0;
+    for (int b = 1; b <= B; ++b) cnt |= mm << (8 * (b - 1));
+    pp.chunk_cnt[s.max_rchunks + i] = cnt;
   }
   for (int i = tid; i < s.n_shared * s.T; i += PM_NT) pp.slot_info[s.P + i] = (i % s.T) | (B << 24);
 }
@@ -320,6 +329,7 @@ hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const in
   pp.pair_slot = reinterpret_cast<int*>(ws + L.pair_slot);
   pp.slot_info = reinterpret_cast<int*>(ws + L.slot_info);
   pp.chunks = reinterpret_cast<int4*>(ws + L.chunks);
+  pp.chunk_cnt = reinterpret_cast<int*>(ws + L.chunk_cnt);
   pp.meta = reinterpret_cast<int*>(ws + L.meta);
   pp.expert_off = reinterpret_cast<int*>(ws + L.expert_off);
   pp.expert_maxbits = reinterpret_cast<int*>(ws + L.expert_maxbits);
