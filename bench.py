@@ -18,7 +18,13 @@ stream around each call, against the algorithmic bytes of that call.  Its
 profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy), used only
 while the kernel sources still hash to the value recorded there.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+With --prefill the same layer runs one T=4096 prefill batch with a
+Zipf(1.1)-skewed expert load (the grouped matrix-core path: chunks of 64
+pairs); that line's roofline is matrix-core bound, in TFLOP/s of the
+routed experts' SwiGLU FFN (6 d f flops per routed pair) against the bf16
+dense peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--prefill]
 """
 from __future__ import annotations
 
@@ -35,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 N_COPIES = 4
 N_XBATCH = 8
 
@@ -88,6 +95,27 @@ def recorded_traffic(T, target):
     return float(rec["traffic_bytes_per_launch"])
 
 
+def read_ceiling(torch, bd, gib=2, reps=10):
+    """Achievable HBM read rate: the library's pure streaming read of a
+    buffer far larger than the 256 MB last-level cache, HIP-event timed."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(bd.STREAM_SINK, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        bd.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        bd.stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def router_bytes(cfg, T):
     return cfg.E * cfg.d * 4 + T * cfg.d * 2 + T * cfg.k * 9
 
@@ -97,6 +125,7 @@ class Layer:
 
     def __init__(self, cfg, w, torch, bd, T):
         self.cfg, self.torch, self.bd, self.T = cfg, torch, bd, T
+        self.bias = torch.from_numpy(w.logit_bias).to("cuda") if w.logit_bias is not None else None
         dev = "cuda"
         base = bd.DeviceBank.from_host(w.routed)
         self.banks = [base] + [base.clone() for _ in range(N_COPIES - 1)]
@@ -115,7 +144,7 @@ class Layer:
         bd, cfg = self.bd, self.cfg
         s = i % N_XBATCH
         bank = self.banks[i % N_COPIES]
-        bd.route(self.xs[s], self.wr, None, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
+        bd.route(self.xs[s], self.wr, self.bias, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
         bd.alloc_bits(self.gate[s].view(-1), cfg.b_lo, cfg.b_max, target, bits=self.bits[s])
         if ev is not None:
             ev[0].record()
@@ -174,7 +203,9 @@ class Layer:
             s = i % N_XBATCH
             b, br, ba, na = algorithmic_ffn_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg)
             nbytes.append(b); bread.append(br); balloc.append(ba); nact.append(na)
-        return dict(ffn_ms=float(np.mean(ffn_ms)), ffn_ms_p10=float(np.percentile(ffn_ms, 10)),
+        cfg = self.cfg
+        flops = 6.0 * cfg.d * cfg.f * self.T * cfg.k  # routed SwiGLU FFN: gate, up, down
+        return dict(ffn_ms=float(np.mean(ffn_ms)), ffn_ms_p10=float(np.percentile(ffn_ms, 10)), ffn_flops=flops,
                     ffn_ms_p50=float(np.percentile(ffn_ms, 50)), ffn_ms_p90=float(np.percentile(ffn_ms, 90)),
                     ffn_bytes=float(np.mean(nbytes)), bits_read=float(np.mean(bread)),
                     bits_alloc=float(np.mean(balloc)), n_active=float(np.mean(nact)))
@@ -215,8 +246,10 @@ def cpu_baseline(cfg, w, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 200; 20 with --prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3 with --prefill)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="the T=4096 Zipf-skewed prefill batch instead of the decode headline")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--target", type=float, default=3.0)
@@ -225,6 +258,10 @@ def main():
                     help="first run a plain device-to-device copy of MIB MiB (a reference dispatch of known "
                          "size for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 20 if args.prefill else 200
+    if args.warmup is None:
+        args.warmup = 3 if args.prefill else 20
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer runs on a single MI355X and has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -246,6 +283,8 @@ def main():
         log(f"copy calibration: 3 x {args.copy_calibration} MiB device copies")
         del src, dst
 
+    if args.prefill:
+        return prefill(args, torch, bd, wl)
     cfg = wl.config(2, T=args.tokens, target=args.target)
     log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
     t0 = time.perf_counter()
@@ -284,6 +323,9 @@ def main():
                 log(f"sweep T={TT} target={tgt}: {TT / ts:.0f} tok/s, FFN {e2['ffn_ms'] * 1e3:.1f} us, "
                     f"{gbs:.0f} GB/s, bits read {e2['bits_read']:.2f}")
 
+    ceiling = read_ceiling(torch, bd)
+    log(f"streaming-read ceiling {ceiling:.0f} GB/s")
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
@@ -313,10 +355,53 @@ def main():
         "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(T, args.target),
+                     "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling,
                      "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
                      "bytes_per_launch": ev["ffn_bytes"]},
         "cpu_baseline": cpu,
         "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def prefill(args, torch, bd, wl):
+    cfg = wl.config(4, target=args.target)
+    T = cfg.T
+    log(f"generating the Qwen3-30B-A3B-shaped layer, prefill T={T} with Zipf-skewed load (seeded)")
+    w = wl.make_workload(cfg, keep_codes=False)
+    L = Layer(cfg, w, torch, bd, T)
+    log(f"timing T={T} target={args.target}: {args.warmup} warmup + {args.steps} graph-replayed steps")
+    t_step = L.timed_graph(args.target, args.steps, args.warmup)
+    ev = L.timed_events(args.target, args.steps)
+    tflops = ev["ffn_flops"] / (ev["ffn_ms"] * 1e-3) / 1e12
+    ceiling = read_ceiling(torch, bd)
+    out = {
+        "metric": "MoE-layer tokens/s, prefill (Qwen3-30B shape)",
+        "value": T / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer, prefill, Zipf(1.1) expert load", "tokens": T,
+                   "hidden": cfg.d, "expert_intermediate": cfg.f, "experts": cfg.E, "top_k": cfg.k,
+                   "bitplanes": cfg.b_max, "group": cfg.g, "b_lo": cfg.b_lo, "target_avg_bits": args.target,
+                   "weight_copies_rotated": N_COPIES, "activation_batches": N_XBATCH},
+        "bits_read": ev["bits_read"],
+        "bits_alloc": ev["bits_alloc"],
+        "n_active_experts": ev["n_active"],
+        "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
+                     "flops_per_launch": ev["ffn_flops"], "hbm_gbs": ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9,
+                     "hbm_read_ceiling_gbs": ceiling},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
+            "moe_stream_read": (i32, [vp, i64, vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
         }
@@ -259,6 +260,19 @@ def residual_to_bf16(h: torch.Tensor, x: Optional[torch.Tensor] = None, stream=N
     st = lib().moe_residual_to_bf16(_ptr(h, torch.float32, "h"), _ptr(x, _BF16, "x"), h.numel(), _stream(stream))
     _check(st, "moe_residual_to_bf16")
     return x
+
+
+STREAM_SINK = 8192
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Pure streaming read of the whole of `buf` (a measurement helper)."""
+    if sink is None:
+        sink = torch.empty(STREAM_SINK, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().moe_stream_read(_ptr(buf, name="buf"), nbytes, sink.data_ptr(), _stream(stream))
+    _check(st, "moe_stream_read")
+    return sink
 
 
 def bf16_tensor(bits_u16: np.ndarray, device="cuda") -> torch.Tensor:

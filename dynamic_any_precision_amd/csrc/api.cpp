@@ -234,4 +234,12 @@ moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* st
   return hip_status(moe::launch_residual_to_bf16(h, x, n, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return MOE_ERR_RANGE;
+  if (bytes == 0) return MOE_OK;
+  if (!buf || !sink) return MOE_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_stream_read(buf, bytes, sink, MOE_STREAM_SINK, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -38,7 +38,40 @@ __global__ __launch_bounds__(256) void k_residual_to_bf16(const float* __restric
   if (i < n) x[i] = (uint16_t)f32_to_bf16(h[i]);
 }
 
+// Streaming read: blocks of 256 threads, 8 loads of 16 B in flight per thread
+// per round, grid-stride.  One XOR-folded word per wave goes to sink.
+constexpr int SR_UNROLL = 8;
+
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ p, int64_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  uint32_t acc = 0u;
+  const int64_t step = (int64_t)gridDim.x * 256 * SR_UNROLL;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * SR_UNROLL + threadIdx.x; base < n16; base += step) {
+    uint4 v[SR_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SR_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n16 ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < SR_UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, WAVE);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int sink_len, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 256 * SR_UNROLL - 1) / (256 * SR_UNROLL);
+  if (blocks > sink_len / 4) blocks = sink_len / 4;
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const uint4*>(buf), n16,
+                     sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream) {
   const size_t total = (size_t)m.N * m.K;

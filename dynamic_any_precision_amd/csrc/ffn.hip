@@ -249,10 +249,15 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
     V += __shfl_xor(V, msk, WAVE);
   }
   const int NQG = a.d / a.g;
-  if ((q & (tpg - 1)) == 0)
+  // 16-pair chunks: rows past the chunk's pairs are never read (the FFN
+  // loads them as out-of-range, i.e. zero), so only live rows are written;
+  // 64-pair chunks copy whole blocks and get zero rows.
+  const bool live = a.sub > 1 || t < m;
+  if ((q & (tpg - 1)) == 0 && live)
     a.xvg[((size_t)c * NQG + kb * (128 / a.g) + q / tpg) * 16 + t] = make_float2(X, V);
   __syncthreads();
-  reinterpret_cast<uint4*>(a.xg + ((size_t)c * (a.d / 128) + kb) * 2048)[tid] = frag[tid];
+  if (a.sub > 1 || (tid & 15) < m)
+    reinterpret_cast<uint4*>(a.xg + ((size_t)c * (a.d / 128) + kb) * 2048)[tid] = frag[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -349,10 +354,10 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   constexpr int SPB = 4 / QPK;
   uint32_t vo_x;
   if (MODE == MODE_W13) {
-    vo_x = (uint32_t)((jg % QPK) * 16 + r16) * 8;
+    vo_x = r16 < m ? (uint32_t)((jg % QPK) * 16 + r16) * 8 : OOB;
   } else {
     const int pidx = (QPK == 1) ? 2 * jg : 4 * (jg & 1) + 2 * (jg >> 1);
-    vo_x = (uint32_t)(r16 * (a.fmax >> 4) + pidx) * 8;
+    vo_x = r16 < m ? (uint32_t)(r16 * (a.fmax >> 4) + pidx) * 8 : OOB;
   }
 
   struct Ops {
@@ -578,7 +583,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
         const float gval = res0[i];
         const float hval = gval / (1.0f + expf(-gval)) * res1[i];
         const float hf = bf16_to_f32(f32_to_bf16(hval));
-        hrow[(4 * jg + i) * 8] = (uint16_t)f32_to_bf16(hf * ainv);
+        if (4 * jg + i < m) hrow[(4 * jg + i) * 8] = (uint16_t)f32_to_bf16(hf * ainv);
         Xp[i] = hf;
         Vp[i] = hf * ainv;
       }
@@ -592,7 +597,8 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
       if (r16 == 0) {
         float2* hs = a.hsg + (size_t)c * a.fmax + u;  // [chunk][token][fmax/16]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hs[(size_t)(4 * jg + i) * (a.fmax >> 4)] = make_float2(Xp[i], Vp[i]);
+        for (int i = 0; i < 4; ++i)
+          if (4 * jg + i < m) hs[(size_t)(4 * jg + i) * (a.fmax >> 4)] = make_float2(Xp[i], Vp[i]);
       }
     }
   } else {

@@ -231,6 +231,19 @@ moe_status moe_dequant(const moe_expert_bank* bank, int32_t expert, int32_t matr
  * from an fp32 residual stream.  n >= 0. */
 moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* stream);
 
+/*
+ * Measurement helper, for callers that compare a kernel's rate with what the
+ * memory system can deliver: a pure streaming read of `bytes` bytes of `buf`
+ * (16-byte loads, every byte read once, nothing else moved), the achievable
+ * HBM read ceiling next to the 8 TB/s specification.  The loaded values are
+ * folded into one uint32 per wave and written to sink[0 .. MOE_STREAM_SINK)
+ * so the loads stay live; their values mean nothing.
+ *   buf   device, 16-byte aligned, bytes a multiple of 16 (bytes >= 0)
+ *   sink  device, MOE_STREAM_SINK uint32 entries, written
+ */
+#define MOE_STREAM_SINK 8192
+moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status status);
 

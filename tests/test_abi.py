@@ -122,6 +122,16 @@ def test_other_entry_points_validate(L):
     assert L.moe_residual_to_bf16(None, None, 0, None) == OK
     assert L.moe_residual_to_bf16(None, fake, 4, None) == NULL
     assert L.moe_residual_to_bf16(fake, fake, -1, None) == RANGE
+
+
+def test_stream_read_validation(L):
+    fake = 256
+    assert L.moe_stream_read(None, 0, None, None) == OK
+    assert L.moe_stream_read(fake, 24, fake, None) == RANGE
+    assert L.moe_stream_read(fake, -16, fake, None) == RANGE
+    assert L.moe_stream_read(None, 16, fake, None) == NULL
+    assert L.moe_stream_read(fake, 16, None, None) == NULL
+    assert L.moe_stream_read(fake + 8, 16, fake, None) == ALIGN
     assert L.moe_permute(fake, fake, 0, 2, 8, 4, fake, fake, fake, fake, 1 << 20, None) == OK
     assert L.moe_permute(fake, fake, 4, 2, 8, 5, fake, fake, fake, fake, 1 << 20, None) == RANGE
     assert L.moe_permute(fake, fake, 4, 2, 8, 4, fake, fake, fake, fake + 1, 1 << 20, None) == ALIGN

@@ -492,3 +492,18 @@ def test_residual_to_bf16_exact():
     ref = orc.round_bf16(h.astype(np.float64))
     got = x.float().cpu().numpy().astype(np.float64)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 2048 * 3 + 48, 1 << 26])
+def test_stream_read_folds_every_word_once(nbytes):
+    # the measurement helper reads every 16-byte word exactly once: the XOR
+    # of its per-wave folds equals the XOR of all 32-bit words of the buffer
+    rng = np.random.default_rng(nbytes % 1000)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(bd.STREAM_SINK, dtype=torch.int32, device="cuda")
+    note(f"stream_read {nbytes} B")
+    bd.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
