@@ -274,8 +274,16 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
 
 constexpr int FFN_THREADS = 256;
 #ifndef FFN_WPE
-#define FFN_WPE 2  // waves per SIMD the kernel is compiled for
+#define FFN_WPE 2  // waves per SIMD the gate/up kernel is compiled for
 #endif
+#ifndef FFN_W2_WPE
+#define FFN_W2_WPE 3  // waves per SIMD of the down kernel (fewer live registers: one k-block ahead)
+#endif
+#ifndef FFN_W2_PF
+#define FFN_W2_PF 1
+#endif
+// waves per SIMD of each kernel (two-group k-blocks keep two: more registers)
+__host__ __device__ constexpr int ffn_wpe(int mode, int qpk) { return (mode == 1 && qpk == 1) ? FFN_W2_WPE : FFN_WPE; }
 #ifndef FFN_PF
 #define FFN_PF 2   // k-blocks in flight ahead of the one being computed (two-tile steps)
 #endif
@@ -294,7 +302,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   constexpr int BM = mask_bmax(MASK);
   constexpr int NT = (MODE == MODE_W13) ? FFN_W13_NT : FFN_W2_NT;  // tiles per step
   constexpr int NP = NT / 2;                                       // gate/up: tile pairs
-  constexpr int PF = (QPK == 2 || CL.n >= 4 || NT > 2) ? 1 : FFN_PF;  // fewer slots where registers are short
+  constexpr int PF = (QPK == 2 || CL.n >= 4 || NT > 2) ? 1 : (ffn_wpe(MODE, QPK) > 2 ? FFN_W2_PF : FFN_PF);  // fewer slots where registers are short
   static_assert(NT % 2 == 0, "tiles per step");
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // token row of the activation operand; weight row of D
@@ -615,7 +623,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
 }
 
 template <int MODE, int QPK>
-__global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(FFN_WPE, FFN_WPE))) void k_ffn(FfnArgs a) {
+__global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn_wpe(MODE, QPK), ffn_wpe(MODE, QPK)))) void k_ffn(FfnArgs a) {
   // Blocks are dealt to the 8 XCDs round-robin (block b on XCD b mod 8);
   // each XCD walks one contiguous eighth of the item list, so a chunk's
   // activations are fetched into at most two XCDs' L2 and an XCD streams
@@ -1093,7 +1101,8 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
   }
   const long max_items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
   long grid = (max_items + 3) / 4;
-  const long cap = (long)num_cu * FFN_WPE;  // FFN_WPE waves per SIMD x 4 SIMDs / 4 waves per block
+  // waves per SIMD x 4 SIMDs / 4 waves per block
+  const long cap = (long)num_cu * ffn_wpe(mode, qpk);
   if (grid > cap) grid = cap;
   grid = (grid + 7) & ~7L;  // whole rounds over the 8 XCDs
   if (mode == MODE_W13) {

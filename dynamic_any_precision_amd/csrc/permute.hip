@@ -183,23 +183,48 @@ __global__ __launch_bounds__(PM_NT) void k_plan_small(FfnShape s, PlanPtrs pp, c
   __shared__ int pre[PM_SMALL_WORDS];
   __shared__ int off[1025];
   __shared__ int wsum[PM_NT / WAVE];
+  __shared__ short sexp[PM_NT * PM_SMALL_PER_T];  // expert of a valid pair, else -1
   __shared__ int errs;
   const int tid = threadIdx.x;
   const int W = s.W, P = s.P, NW = s.E * s.B * W;
   for (int j = tid; j < NW; j += PM_NT) bm[j] = 0u;
   if (tid == 0) errs = 0;
+  int err = 0;
+  int bw[PM_SMALL_PER_T];
+#pragma unroll
+  for (int r = 0; r < PM_SMALL_PER_T; ++r) {
+    const int i = tid + r * PM_NT;
+    bw[r] = 0;
+    if (i < P) {
+      const int e = idx[i], b = bits[i];
+      const bool ok = e >= 0 && e < s.E && b >= 1 && b <= s.B;
+      if (!ok) err |= 1;
+      sexp[i] = (short)(ok ? e : -1);
+      bw[r] = b;
+    }
+  }
   __syncthreads();
 
+  // key of each pair; an earlier valid pair of the token with the same
+  // expert drops it
   int keys[PM_SMALL_PER_T];
-  int err = 0;
 #pragma unroll
   for (int r = 0; r < PM_SMALL_PER_T; ++r) {
     const int i = tid + r * PM_NT;
     keys[r] = -1;
     if (i < P) {
-      keys[r] = pair_key(s, idx, bits, i, err);
-      const int t = i / s.k;
-      if (keys[r] >= 0) atomicOr(&bm[keys[r] * W + (t >> 5)], 1u << (t & 31));
+      const int e = sexp[i];
+      if (e >= 0) {
+        bool dup = false;
+        for (int j = (i / s.k) * s.k; j < i; ++j) dup |= sexp[j] == e;
+        if (dup) {
+          err |= 2;
+        } else {
+          keys[r] = e * s.B + (s.B - bw[r]);
+          const int t = i / s.k;
+          atomicOr(&bm[keys[r] * W + (t >> 5)], 1u << (t & 31));
+        }
+      }
     }
   }
   if (err) atomicOr(&errs, err);
