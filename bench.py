@@ -9,8 +9,9 @@ combine.  Inputs are resident in HBM before timing; four copies of the
 expert bank (1.36 GB) are rotated and eight activation batches cycled so the
 256 MB last-level cache can not serve the weights.
 
-The headline step runs T=32 tokens at target 3.0 bits, replayed from HIP
-graphs; a sweep over T in {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
+The headline step is one moe_layer call (the whole layer; at decode sizes
+its softmax + top-k, allocation and plan run as one single-block kernel) on
+T=32 tokens at target 3.0 bits, replayed from HIP graphs; a sweep over T in {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
 The roofline object is for the FFN stage (moe_anyprec_ffn: plan, activation
 gather, gate/up + SwiGLU, down, combine), timed with HIP events on its
 stream around each call, against the algorithmic bytes of that call.  Its
@@ -134,6 +135,7 @@ class Layer:
         self.wr = torch.from_numpy(w.w_router).to(dev)
         self.rws = bd.route_workspace(T, cfg.E)
         self.fws = bd.ffn_workspace(base, None, T, cfg.k)
+        self.lws = bd.layer_workspace(base, None, T, cfg.k)
         self.idx = [torch.empty(T, cfg.k, dtype=torch.int32, device=dev) for _ in range(N_XBATCH)]
         self.gate = [torch.empty(T, cfg.k, dtype=torch.float32, device=dev) for _ in range(N_XBATCH)]
         self.bits = [torch.empty(T * cfg.k, dtype=torch.uint8, device=dev) for _ in range(N_XBATCH)]
@@ -141,17 +143,21 @@ class Layer:
         self.graphs = {}
 
     def step(self, i, target, ev=None):
+        """One layer step: moe_layer (one call), or with ev the three calls
+        route, alloc, FFN with HIP events around the FFN call."""
         bd, cfg = self.bd, self.cfg
         s = i % N_XBATCH
         bank = self.banks[i % N_COPIES]
+        if ev is None:
+            bd.layer(bank, None, self.xs[s], self.wr, self.bias, cfg.k, cfg.b_lo, target, y=self.y, idx=self.idx[s],
+                     gate=self.gate[s], bits=self.bits[s], workspace=self.lws)
+            return
         bd.route(self.xs[s], self.wr, self.bias, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
         bd.alloc_bits(self.gate[s].view(-1), cfg.b_lo, cfg.b_max, target, bits=self.bits[s])
-        if ev is not None:
-            ev[0].record()
+        ev[0].record()
         bd.anyprec_ffn(bank, None, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
                        workspace=self.fws)
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
 
     def capture(self, target):
         torch = self.torch
@@ -191,8 +197,9 @@ class Layer:
         """Eager steps; HIP events around each FFN call on the current stream."""
         torch = self.torch
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(N_XBATCH)]
         for i in range(N_XBATCH):
-            self.step(i, target)
+            self.step(i, target, warm[i])
         torch.cuda.synchronize()
         for i in range(steps):
             self.step(i, target, evs[i])

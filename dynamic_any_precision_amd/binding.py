@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
             "moe_ffn_workspace_bytes": (sz, [bp, bp, i32, i32]),
             "moe_anyprec_ffn": (i32, [bp, bp, vp, i32, i32, vp, vp, vp, vp, i32, vp, sz, vp]),
             "moe_permute": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_layer_workspace_bytes": (sz, [bp, bp, i32, i32]),
+            "moe_layer": (i32, [bp, bp, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp, sz, vp]),
             "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
             "moe_stream_read": (i32, [vp, i64, vp, vp]),
@@ -232,6 +234,41 @@ def anyprec_ffn(routed: DeviceBank, shared: Optional[DeviceBank], x: torch.Tenso
                                _stream(stream))
     _check(st, "moe_anyprec_ffn")
     return y
+
+
+def layer_workspace(routed: DeviceBank, shared: Optional[DeviceBank], T: int, top_k: int, device="cuda"):
+    n = int(lib().moe_layer_workspace_bytes(ctypes.byref(routed.struct()), _bank_struct(shared), T, top_k))
+    if n == 0 and T > 0:
+        raise MoeError(2, "moe_layer_workspace_bytes", "invalid bank or sizes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def layer(routed: DeviceBank, shared: Optional[DeviceBank], x: torch.Tensor, w_router: torch.Tensor,
+          logit_bias: Optional[torch.Tensor], top_k: int, b_lo: int, target: float, renorm: bool = False,
+          y: Optional[torch.Tensor] = None, accumulate: bool = False, idx: Optional[torch.Tensor] = None,
+          gate: Optional[torch.Tensor] = None, bits: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None, stream=None):
+    """The whole layer (route, allocate, FFN) in one call; returns y, idx, gate, bits."""
+    T, d = x.shape
+    dev = x.device
+    if workspace is None:
+        workspace = layer_workspace(routed, shared, T, top_k, dev)
+    if y is None:
+        y = torch.zeros(T, d, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    if gate is None:
+        gate = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+    if bits is None:
+        bits = torch.empty(T * top_k, dtype=torch.uint8, device=dev)
+    st = lib().moe_layer(ctypes.byref(routed.struct()), _bank_struct(shared), _ptr(x, _BF16, "x"), T, top_k,
+                         _ptr(w_router, torch.float32, "w_router"), _ptr(logit_bias, torch.float32, "logit_bias"),
+                         int(renorm), b_lo, float(target), _ptr(idx, torch.int32, "topk_idx"),
+                         _ptr(gate, torch.float32, "topk_gate"), _ptr(bits, torch.uint8, "bits"),
+                         _ptr(y, torch.float32, "y"), int(accumulate), _ptr(workspace, name="workspace"),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_layer")
+    return y, idx, gate, bits
 
 
 def permute(idx: torch.Tensor, bits: torch.Tensor, E: int, b_max: int, workspace: torch.Tensor, stream=None):

@@ -104,6 +104,25 @@ moe_status ffn_shape(const moe_expert_bank* routed, const moe_expert_bank* share
   return MOE_OK;
 }
 
+// The FFN after the plan: activation gather, gate/up + SwiGLU, down, combine.
+hipError_t ffn_after_plan(const moe::FfnShape& s, const moe::FfnLayout& L, char* ws, const moe_expert_bank* routed,
+                          const moe_expert_bank* shared, const uint16_t* x, const float* topk_gate, float* y,
+                          int32_t accumulate, hipStream_t strm) {
+  const int ncu = num_cu_cached();
+  moe::MatrixDev none;
+  std::memset(&none, 0, sizeof(none));
+  none.N = 16;
+  none.K = 128;
+  hipError_t e = moe::launch_gather(s, L, ws, x, strm);
+  if (e == hipSuccess)
+    e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = moe::launch_ffn_w2(s, L, ws, w2_of(routed), shared ? w2_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = moe::launch_combine(s, L, ws, topk_gate, y, accumulate, strm);
+  return e;
+}
+
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
 }  // namespace
 
 extern "C" {
@@ -178,17 +197,54 @@ moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank*
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const int ncu = num_cu_cached();
-  moe::MatrixDev none;
-  std::memset(&none, 0, sizeof(none));
-  none.N = 16;
-  none.K = 128;
   hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
-  if (e == hipSuccess) e = moe::launch_gather(s, L, ws, x, strm);
-  if (e == hipSuccess)
-    e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
-  if (e == hipSuccess) e = moe::launch_ffn_w2(s, L, ws, w2_of(routed), shared ? w2_of(shared) : none, ncu, strm);
-  if (e == hipSuccess) e = moe::launch_combine(s, L, ws, topk_gate, y, accumulate, strm);
+  if (e == hipSuccess) e = ffn_after_plan(s, L, ws, routed, shared, x, topk_gate, y, accumulate, strm);
+  return hip_status(e);
+}
+
+size_t moe_layer_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T,
+                                 int32_t top_k) {
+  moe::FfnShape s;
+  if (ffn_shape(routed, shared, T, top_k, false, &s) != MOE_OK) return 0;
+  return al256(moe::make_layout(s).total) + moe::route_workspace_bytes(T, routed->n_experts);
+}
+
+moe_status moe_layer(const moe_expert_bank* routed, const moe_expert_bank* shared, const uint16_t* x, int32_t T,
+                     int32_t top_k, const float* w_router, const float* logit_bias, int32_t renorm_topk,
+                     int32_t b_lo, float target_avg_bits, int32_t* topk_idx, float* topk_gate, uint8_t* bits,
+                     float* y, int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  moe::FfnShape s;
+  moe_status st = ffn_shape(routed, shared, T, top_k, true, &s);
+  if (st != MOE_OK) return st;
+  const int32_t b_max = routed->b_max;
+  if (b_lo < 1 || b_lo > b_max) return MOE_ERR_RANGE;
+  if (!(target_avg_bits >= (float)b_lo && target_avg_bits <= (float)b_max)) return MOE_ERR_RANGE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate || !bits || !y || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+    return MOE_ERR_ALIGN;
+  const moe::FfnLayout L = moe::make_layout(s);
+  const size_t route_off = al256(L.total);
+  if (ws_bytes < route_off + moe::route_workspace_bytes(T, s.E)) return MOE_ERR_WORKSPACE;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  double* logits = reinterpret_cast<double*>(ws + route_off);
+  const int32_t n_star = exact_budget(s.P, b_lo, b_max, target_avg_bits);
+  hipError_t e = moe::launch_route_logits(x, T, s.d, w_router, s.E, logit_bias, logits, strm);
+  if (e == hipSuccess) {
+    if (moe::control_fits(s)) {
+      if (!moe::control_does_topk(s))
+        e = moe::launch_route_topk(logits, T, s.E, top_k, renorm_topk, topk_idx, topk_gate, strm);
+      if (e == hipSuccess)
+        e = moe::launch_control(s, L, ws, logits, renorm_topk, n_star, b_lo, b_max, topk_idx, topk_gate, bits,
+                                strm);
+    } else {
+      e = moe::launch_route_topk(logits, T, s.E, top_k, renorm_topk, topk_idx, topk_gate, strm);
+      if (e == hipSuccess) e = moe::launch_alloc(topk_gate, s.P, n_star, b_lo, b_max, bits, nullptr, nullptr, strm);
+      if (e == hipSuccess) e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
+    }
+  }
+  if (e == hipSuccess) e = ffn_after_plan(s, L, ws, routed, shared, x, topk_gate, y, accumulate, strm);
   return hip_status(e);
 }
 

@@ -11,6 +11,10 @@ namespace moe {
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const uint16_t* x, int T, int d, const float* W, int E, const float* bias, int k,
                         int renorm, int* idx, float* gate, void* ws, hipStream_t stream);
+hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, int E, const float* bias,
+                               double* logits, hipStream_t stream);
+hipError_t launch_route_topk(const double* logits, int T, int E, int k, int renorm, int* idx, float* gate,
+                             hipStream_t stream);
 
 // ---- allocation
 hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_max, uint8_t* bits, float* tau_out,
@@ -50,6 +54,13 @@ struct MatrixDev {
 // Plan: permutation, histogram, chunks.
 hipError_t launch_plan(const FfnShape& s, const FfnLayout& L, char* ws, const int* idx, const uint8_t* bits,
                        hipStream_t stream);
+// Fused decode control (softmax + top-k, allocation, plan) in one block.
+struct FfnLayout;
+bool control_fits(const FfnShape& s);
+bool control_does_topk(const FfnShape& s);
+hipError_t launch_control(const FfnShape& s, const FfnLayout& L, char* ws, const double* logits, int renorm,
+                          int n_star, int b_lo, int b_max, int* idx, float* gate, uint8_t* bits,
+                          hipStream_t stream);
 // Activation fragments of every chunk (after the plan).
 hipError_t launch_gather(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream);
 hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,

@@ -11,6 +11,7 @@
 // desc, index asc) through DPP lane moves.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
@@ -41,102 +42,14 @@ __device__ __forceinline__ void butterfly32(double (&v)[32], int lane) {
   v[0] += __shfl_xor(v[0], 32, WAVE);
 }
 
-// Order-preserving map of a double to an unsigned 64-bit key (larger logit,
-// larger key; -0 and +0 equal).  Logits are finite.
-__device__ __forceinline__ uint64_t order_key64(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
-// (key, index) a beats (key, index) b: larger logit, then smaller index.
-__device__ __forceinline__ bool beats(uint64_t ka, int ia, uint64_t kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
-// One step of the wave arg-max: each lane takes the better of its own
-// candidate and the candidate DPP control CTRL moves to it (lanes with no
-// source keep their own).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void argmax_step(uint32_t& hi, uint32_t& lo, int& ix) {
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
-  const int oix = __builtin_amdgcn_update_dpp(ix, ix, CTRL, ROWS, 0xF, false);
-  const uint64_t ok = ((uint64_t)ohi << 32) | olo, mk = ((uint64_t)hi << 32) | lo;
-  if (beats(ok, oix, mk, ix)) {
-    hi = ohi;
-    lo = olo;
-    ix = oix;
-  }
-}
-
-// Softmax over the E logits of one token and its top k, by one wave: k
-// rounds of a wave-wide arg-max; lane l owns experts l, l+64, l+128, l+192.
-// The arg-max shifts candidates right by 1, 2, 4, 8 lanes within each row of
-// 16 and then carries rows 0 and 2 into rows 1 and 3 (row broadcast 15) and
-// row 1 into rows 2 and 3 (row broadcast 31): lane 63 ends with the winner.
-__device__ void topk_token(const double* __restrict__ lg, int E, int k, int renorm, int* __restrict__ idx_out,
-                           float* __restrict__ gate_out, int lane) {
-  double lv[4];
-  uint64_t key[4];
-  bool avail[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    avail[i] = e < E;
-    lv[i] = avail[i] ? lg[e] : 0.0;
-    key[i] = avail[i] ? order_key64(lv[i]) : 0ull;
-  }
-  double mx = 0.0, ps = 0.0, psel = 0.0;
-  int my_e = 0;        // lane r keeps the winner of round r
-  double my_l = 0.0;
-  for (int r = 0; r < k; ++r) {
-    uint64_t bk = 0ull;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (avail[i] && beats(key[i], lane + 64 * i, bk, be)) {
-        bk = key[i];
-        be = lane + 64 * i;
-      }
-    uint32_t hi = (uint32_t)(bk >> 32), lo = (uint32_t)bk;
-    argmax_step<0x111, 0xF>(hi, lo, be);  // row_shr:1
-    argmax_step<0x112, 0xF>(hi, lo, be);  // row_shr:2
-    argmax_step<0x114, 0xF>(hi, lo, be);  // row_shr:4
-    argmax_step<0x118, 0xF>(hi, lo, be);  // row_shr:8
-    argmax_step<0x142, 0xA>(hi, lo, be);  // row_bcast:15
-    argmax_step<0x143, 0xC>(hi, lo, be);  // row_bcast:31
-    be = __builtin_amdgcn_readlane(be, 63);
-    // the owner retires the winner
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (be == lane + 64 * i) avail[i] = false;
-    const double bl = lg[be];
-    if (lane == r) {
-      my_e = be;
-      my_l = bl;
-    }
-    if (r == 0) {
-      mx = bl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i < E) ps += exp(lv[i] - mx);
-      ps = wave_sum_d(ps);
-    }
-    psel += exp(bl - mx) / ps;
-  }
-  if (lane < k) {
-    const double p = exp(my_l - mx) / ps;
-    idx_out[lane] = my_e;
-    gate_out[lane] = (float)(renorm ? p / psel : p);
-  }
-}
-
 // One wave per token.
 __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int k, int renorm,
                                                     int* __restrict__ idx_out, float* __restrict__ gate_out) {
   const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
   if (t >= T) return;
-  topk_token(logits + (size_t)t * E, E, k, renorm, idx_out + (size_t)t * k, gate_out + (size_t)t * k,
+  int* io = idx_out + (size_t)t * k;
+  float* go = gate_out + (size_t)t * k;
+  topk_token(logits + (size_t)t * E, E, k, renorm, [&](int j, int e, float g) { io[j] = e; go[j] = g; },
              threadIdx.x & 63);
 }
 
@@ -205,13 +118,25 @@ size_t route_workspace_bytes(int T, int E) {
   return ((size_t)T * E * sizeof(double) + 255) & ~size_t(255);
 }
 
+hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, int E, const float* bias,
+                               double* logits, hipStream_t stream) {
+  dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
+  hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_topk(const double* logits, int T, int E, int k, int renorm, int* idx, float* gate,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, renorm, idx, gate);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const uint16_t* x, int T, int d, const float* W, int E, const float* bias, int k,
                         int renorm, int* idx, float* gate, void* ws, hipStream_t stream) {
   double* logits = static_cast<double*>(ws);
-  dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
-  hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
-  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, renorm, idx, gate);
-  return hipGetLastError();
+  hipError_t e = launch_route_logits(x, T, d, W, E, bias, logits, stream);
+  if (e == hipSuccess) e = launch_route_topk(logits, T, E, k, renorm, idx, gate, stream);
+  return e;
 }
 
 }  // namespace moe

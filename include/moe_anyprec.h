@@ -200,6 +200,28 @@ moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank*
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The whole layer in one call: moe_route (without a separate workspace),
+ * moe_alloc_bits over the call's T*top_k routed pairs, then moe_anyprec_ffn,
+ * with the same results as those three calls in sequence (the passages they
+ * cite).  For decode-sized batches (T*top_k <= 1024 and
+ * n_experts*b_max*ceil(T/32) <= 4096) the allocation and the FFN's plan run
+ * as one single-block kernel, with the softmax + top-k too when T <= 16.
+ *   x, w_router, logit_bias, renorm_topk   as for moe_route (d = routed->d_model,
+ *                                          E = routed->n_experts)
+ *   b_lo, target_avg_bits                  as for moe_alloc_bits (b_max = routed->b_max)
+ *   topk_idx [T][top_k], topk_gate [T][top_k], bits [T*top_k]   outputs, device
+ *   y, accumulate                          as for moe_anyprec_ffn
+ *   workspace  >= moe_layer_workspace_bytes(...), 256-byte aligned, any content
+ * Ranges and errors: those of the three calls.
+ */
+size_t moe_layer_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T,
+                                 int32_t top_k);
+moe_status moe_layer(const moe_expert_bank* routed, const moe_expert_bank* shared, const uint16_t* x, int32_t T,
+                     int32_t top_k, const float* w_router, const float* logit_bias, int32_t renorm_topk,
+                     int32_t b_lo, float target_avg_bits, int32_t* topk_idx, float* topk_gate, uint8_t* bits,
+                     float* y, int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * The token-to-expert permutation and histogram step of moe_anyprec_ffn, on
  * its own, for inspection.  Pairs are ordered stably by (expert ascending,
  * bits descending, pair id ascending), pair id = t*top_k + j.

@@ -136,3 +136,22 @@ def test_stream_read_validation(L):
     assert L.moe_permute(fake, fake, 4, 2, 8, 5, fake, fake, fake, fake, 1 << 20, None) == RANGE
     assert L.moe_permute(fake, fake, 4, 2, 8, 4, fake, fake, fake, fake + 1, 1 << 20, None) == ALIGN
     assert L.moe_permute(fake, fake, 4, 2, 8, 4, fake, fake, fake, fake, 16, None) == WS
+
+
+def test_layer_validation(L):
+    fake = 256
+    b = _bank()
+    args = lambda **kw: [ctypes.byref(kw.get("bank", b)), None, kw.get("x", fake), kw.get("T", 4), kw.get("k", 2),
+                         kw.get("wr", fake), None, 0, kw.get("b_lo", 2), kw.get("tgt", 3.0), fake, fake, fake,
+                         kw.get("y", fake), 0, kw.get("ws", fake), kw.get("wsb", 1 << 30), None]
+    assert L.moe_layer(*args(T=0)) == OK
+    assert L.moe_layer(*args(x=None)) == NULL
+    assert L.moe_layer(*args(wr=None)) == NULL
+    assert L.moe_layer(*args(b_lo=0)) == RANGE
+    assert L.moe_layer(*args(tgt=4.5)) == RANGE
+    assert L.moe_layer(*args(tgt=1.5)) == RANGE
+    assert L.moe_layer(*args(k=9)) == RANGE
+    assert L.moe_layer(*args(ws=fake + 16)) == ALIGN
+    need = L.moe_layer_workspace_bytes(ctypes.byref(b), None, 4, 2)
+    assert need > L.moe_ffn_workspace_bytes(ctypes.byref(b), None, 4, 2)
+    assert L.moe_layer(*args(wsb=need - 1)) == WS

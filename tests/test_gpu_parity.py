@@ -507,3 +507,27 @@ def test_stream_read_folds_every_word_once(nbytes):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+# ---------------------------------------------------------------------------
+# the whole layer in one call: identical to route + alloc + FFN in sequence
+
+
+@pytest.mark.parametrize("case", [(1, {}), (1, dict(T=100)), (1, dict(T=300)), (2, dict(T=1)), (2, {}),
+                                  (2, dict(T=128)), (3, {}), (3, dict(b_lo=1)), (4, dict(T=512))])
+def test_layer_call_equals_three_calls(case):
+    i, over = case
+    w, dev, _, _ = workload(i, **over)
+    cfg = w.cfg
+    x = dev["x"]
+    note(f"layer cfg{i} {over}")
+    idx, gate = bd.route(x, dev["w_router"], dev["bias"], cfg.k)
+    bits = bd.alloc_bits(gate.reshape(-1), cfg.b_lo, 4, cfg.target)
+    y_ref = bd.anyprec_ffn(dev["routed"], dev["shared"], x, idx, gate, bits)
+    y, idx2, gate2, bits2 = bd.layer(dev["routed"], dev["shared"], x, dev["w_router"], dev["bias"], cfg.k,
+                                     cfg.b_lo, cfg.target)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx)
+    assert torch.equal(gate2, gate)
+    assert torch.equal(bits2, bits)
+    assert torch.equal(y, y_ref)
