@@ -10,8 +10,10 @@ expert bank (1.36 GB) are rotated and eight activation batches cycled so the
 256 MB last-level cache can not serve the weights.
 
 The headline step is one moe_layer call (the whole layer; at decode sizes
-its softmax + top-k, allocation and plan run as one single-block kernel) on
-T=32 tokens at target 3.0 bits, replayed from HIP graphs; a sweep over T in {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
+its allocation and plan run as one single-block kernel, with the top-k too
+for T <= 16) on T=32 tokens at target 3.0 bits, replayed from HIP graphs
+that each hold one cycle of the 8 activation batches; a sweep over T in
+{1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
 The roofline object is for the FFN stage (moe_anyprec_ffn: plan, activation
 gather, gate/up + SwiGLU, down, combine), timed with HIP events on its
 stream around each call, against the algorithmic bytes of that call.  Its
@@ -159,9 +161,10 @@ class Layer:
                        workspace=self.fws)
         ev[1].record()
 
-    def capture(self, target):
+    def capture(self, target, nsteps=N_XBATCH):
+        """HIP graph of steps 0 .. nsteps-1 of a cycle (nsteps <= N_XBATCH)."""
         torch = self.torch
-        key = float(target)
+        key = (float(target), nsteps)
         if key in self.graphs:
             return self.graphs[key]
         gs = []
@@ -172,24 +175,29 @@ class Layer:
                 self.step(i, target)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for i in range(N_XBATCH):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nsteps):
                 self.step(i, target)
-            gs.append(g)
+        gs.append(g)
         torch.cuda.synchronize()
         self.graphs[key] = gs
         return gs
 
     def timed_graph(self, target, steps, warmup):
         torch = self.torch
-        gs = self.capture(target)
-        for i in range(warmup):
-            gs[i % N_XBATCH].replay()
+        # one graph per cycle of N_XBATCH steps, plus one for the remainder:
+        # exactly `steps` steps are timed
+        full = self.capture(target)[0]
+        rem = self.capture(target, steps % N_XBATCH)[0] if steps % N_XBATCH else None
+        for i in range(max(1, -(-warmup // N_XBATCH))):
+            full.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            gs[i % N_XBATCH].replay()
+        for i in range(steps // N_XBATCH):
+            full.replay()
+        if rem is not None:
+            rem.replay()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 

@@ -2,11 +2,11 @@
 // top-k.  ("routing each token to a small set of experts", DPA-MoE abstract;
 // "routing scores", MatMoE abstract.)
 //
-// Logits: grid (E/8 expert tiles, T/4 token tiles), 256 threads.  The four
-// waves of a block split the hidden dimension; each accumulates the 8 x 4
+// Logits: grid (E/4 expert tiles, T/8 token tiles), 512 threads.  The eight
+// waves of a block split the hidden dimension; each accumulates the 4 x 8
 // (expert, token) dot products of its slice in float64 from exact bf16 /
 // fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
-// pair l, and wave 0 adds the four slices in a fixed order.
+// pair l, and wave 0 adds the eight slices in a fixed order.
 // Top-k: one wave per token, k rounds of a wave-wide arg-max over (logit
 // desc, index asc) through DPP lane moves.
 #include "common.hpp"
@@ -17,9 +17,9 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_TT = 4;  // tokens per block (one wave each for top-k)
-constexpr int RT_ET = 8;  // experts per block
-constexpr int RT_WAVES = 4;
+constexpr int RT_TT = 8;  // tokens per block
+constexpr int RT_ET = 4;  // experts per block
+constexpr int RT_WAVES = 8;
 
 template <int M, int N>
 __device__ __forceinline__ void butterfly_step(double (&v)[N], int lane) {
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
              threadIdx.x & 63);
 }
 
-__global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ x, int T, int d,
+__global__ __launch_bounds__(RT_WAVES * 64) void k_route_logits(const uint16_t* __restrict__ x, int T, int d,
                                                       const float* __restrict__ W, int E,
                                                       const float* __restrict__ bias, double* __restrict__ logits) {
   __shared__ double part[RT_WAVES][64];
@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
     const int ee = lane / RT_TT, tt = lane % RT_TT;
     const int e = e0 + ee, t = t0 + tt;
     if (e < E && tt < nt) {
-      double l = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+      double l = part[0][lane];
+#pragma unroll
+      for (int w = 1; w < RT_WAVES; ++w) l += part[w][lane];
       if (bias) l += (double)bias[e];
       logits[(size_t)t * E + e] = l;
     }
@@ -121,7 +123,7 @@ size_t route_workspace_bytes(int T, int E) {
 hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, int E, const float* bias,
                                double* logits, hipStream_t stream) {
   dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
-  hipLaunchKernelGGL(k_route_logits, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
+  hipLaunchKernelGGL(k_route_logits, grid, dim3(RT_WAVES * 64), 0, stream, x, T, d, W, E, bias, logits);
   return hipGetLastError();
 }
 
