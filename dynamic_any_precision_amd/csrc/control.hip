@@ -4,7 +4,9 @@
 // (route_dev.hpp, alloc.hip, plan_dev.hpp); it saves launches and round trips
 // through memory between them.  With more tokens than the block has waves
 // the top-k runs as its own kernel (one wave per token across the chip) and
-// this kernel takes its output: allocation and plan only.
+// this kernel takes its output: allocation and plan only.  Here the top-k
+// ranks every (token, expert) candidate across the block instead of k
+// arg-max rounds per token.
 //
 // Allocation by ranks: with n* the budget, the threshold tau of the
 // bisection (the smallest key whose strict upper set holds at most n*
@@ -24,6 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int CTL_MAX_PAIRS = PM_NT;
+constexpr int CTL_TOPK_TOKENS = PM_NT / WAVE;  // tokens up to which the top-k runs here
 
 __device__ __forceinline__ uint32_t gate_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -49,25 +52,74 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
       skey[i] = gate_key(gate_out[i]);
     }
   }
-  // softmax + top-k: one wave per token, tokens dealt round-robin
-  for (int t = wave; TOPK && t < s.T; t += PM_NT / WAVE) {
-    const int base = t * s.k;
-    topk_token(logits + (size_t)t * s.E, s.E, s.k, renorm,
-               [&](int j, int e, float g) {
-                 idx_out[base + j] = e;
-                 gate_out[base + j] = g;
-                 L.sexp[base + j] = (short)e;
-                 skey[base + j] = gate_key(g);
-               },
-               lane);
+  if (TOPK) {
+    // Top-k by ranks over the whole block: the rank of candidate (t, e) is
+    // the number of the token's experts that beat it (larger logit, then
+    // smaller index), so rank r is round r of the one-wave arg-max.  Then
+    // one wave per token forms the softmax exactly as the top-k kernel does.
+    __shared__ uint64_t ckey[CTL_TOPK_TOKENS * 256];
+    __shared__ double wl[CTL_TOPK_TOKENS * 8];
+    __shared__ int we[CTL_TOPK_TOKENS * 8];
+    const int TE = s.T * s.E;
+    for (int c = tid; c < TE; c += PM_NT) ckey[c] = order_key64(logits[c]);
+    __syncthreads();
+    for (int c = tid; c < TE; c += PM_NT) {
+      const int t = c / s.E, e = c - t * s.E;
+      const uint64_t kv = ckey[c];
+      const uint64_t* kt = ckey + t * s.E;
+      int rank = 0;
+      for (int j = 0; j < s.E; ++j) {
+        const uint64_t kj = kt[j];
+        rank += (kj > kv || (kj == kv && j < e)) ? 1 : 0;
+      }
+      if (rank < s.k) {
+        we[t * 8 + rank] = e;
+        wl[t * 8 + rank] = key_to_double(kv);
+      }
+    }
+    __syncthreads();
+    for (int t = wave; t < s.T; t += PM_NT / WAVE) {
+      const uint64_t* kt = ckey + t * s.E;
+      const double mx = wl[t * 8];
+      double ps = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < s.E) ps += exp(key_to_double(kt[lane + 64 * i]) - mx);
+      ps = wave_sum_d(ps);
+      const double p = lane < s.k ? exp(wl[t * 8 + (lane < s.k ? lane : 0)] - mx) / ps : 0.0;
+      double psel = 0.0;
+      if (renorm) {
+        const long long pb = __double_as_longlong(p);
+        for (int r = 0; r < s.k; ++r) {
+          const int lo = __builtin_amdgcn_readlane((int)(uint32_t)pb, r);
+          const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), r);
+          psel += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+        }
+      }
+      if (lane < s.k) {
+        const int base = t * s.k, e = we[t * 8 + lane];
+        const float g = (float)(renorm ? p / psel : p);
+        idx_out[base + lane] = e;
+        gate_out[base + lane] = g;
+        L.sexp[base + lane] = (short)e;
+        skey[base + lane] = gate_key(g);
+      }
+    }
   }
   __syncthreads();
 
-  // allocation: high width iff #{keys >= own key} <= n*
+  // allocation: high width iff #{keys >= own key} <= n*; the keys past P
+  // (up to a multiple of 8) read as 0, below every gate key
+  for (int j = s.P + tid; j < ((s.P + 7) & ~7); j += PM_NT) skey[j] = 0u;
+  __syncthreads();
   if (tid < s.P) {
     const uint32_t v = skey[tid];
     int ge = 0;
-    for (int j = 0; j < s.P; ++j) ge += skey[j] >= v ? 1 : 0;
+    const uint4* k4 = reinterpret_cast<const uint4*>(skey);
+    for (int j = 0; j < (s.P + 7) / 8; ++j) {
+      const uint4 a = k4[2 * j], b = k4[2 * j + 1];
+      ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
+    }
     const int b = ge <= n_star ? b_max : b_lo;
     bits_out[tid] = (uint8_t)b;
     L.sbits[tid] = (uint8_t)b;
@@ -85,7 +137,7 @@ bool control_fits(const FfnShape& s) {
 }
 
 // the top-k inside the control kernel while every token has a wave of its own
-bool control_does_topk(const FfnShape& s) { return s.T <= PM_NT / WAVE; }
+bool control_does_topk(const FfnShape& s) { return s.T <= CTL_TOPK_TOKENS; }
 
 hipError_t launch_control(const FfnShape& s, const FfnLayout& L, char* ws, const double* logits, int renorm,
                           int n_star, int b_lo, int b_max, int* idx, float* gate, uint8_t* bits,

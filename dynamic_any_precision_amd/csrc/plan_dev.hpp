@@ -153,7 +153,7 @@ __device__ __forceinline__ void put_slot(const FfnShape& s, const PlanPtrs& pp, 
 
 // LDS of the one-block plan.  The caller fills sexp (expert of a valid pair,
 // else -1) and sbits (its width) for every pair.
-struct PlanSmallLds {
+struct alignas(16) PlanSmallLds {
   uint32_t bm[PM_SMALL_WORDS];
   int pre[PM_SMALL_WORDS];
   int off[1025];
