@@ -294,9 +294,20 @@ __host__ __device__ constexpr int ffn_wpe(int mode, int qpk) { return (mode == 1
 #define FFN_W2_NT 2   // down tiles per step
 #endif
 
+// The next item's chunk record, loaded while an item streams
+// (vector registers, every lane the same) and made scalar once the stream's
+// own waits have covered them, before the item's output stores.
+struct NextRec {
+  u32x4_t ch;
+  uint32_t cnt;
+};
+struct NextVal {
+  int e, s0, m, mask, cnt;
+};
+
 template <int MODE, int QPK, int MASK>
 __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, int c, int e, int s0, int m,
-                                         int cnt, int item) {
+                                         int cnt, int item, const NextRec& nr, NextVal& nv) {
   constexpr Units U = make_units(MASK);
   constexpr Classes CL = make_classes(MASK);
   constexpr int BM = mask_bmax(MASK);
@@ -571,6 +582,11 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   for (int q = 0; q < PF; ++q)
     if (j0 + q < NJ) compute(o[q], j0 + q);
   if (STAGGER) tile_scale(accb[1], sprev, out[NT - 1]);
+  nv.e = uniform((int)nr.ch[0]);
+  nv.s0 = uniform((int)nr.ch[1]);
+  nv.m = uniform((int)nr.ch[2]);
+  nv.mask = uniform((int)nr.ch[3]);
+  nv.cnt = uniform((int)nr.cnt);
 
   if (MODE == MODE_W13) {
 #pragma unroll
@@ -628,61 +644,83 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
   // each XCD walks one contiguous eighth of the item list, so a chunk's
   // activations are fetched into at most two XCDs' L2 and an XCD streams
   // few experts' planes at a time.  (The mapping only affects where work
-  // runs, not what it computes.)  The next item's chunk record loads while
-  // the current item streams.
+  // runs, not what it computes.)  Wave l of an XCD takes items l, l + n,
+  // l + 2n, ... of the XCD's range (n waves per XCD).  The next item's chunk
+  // record is loaded before the current item streams and read after it.
   const int xcd = blockIdx.x & 7;
   const int lw = uniform((int)(((blockIdx.x >> 3) * blockDim.x + threadIdx.x) >> 6));
   const int nlw = (int)(((gridDim.x >> 3) * blockDim.x) >> 6);
   const int items_r = a.meta[0] * a.items[0];
   const int items = items_r + a.n_schunks * a.items[1];
-  struct Item {
-    int c, item, sh;
-    u32x4_t ch;    // chunk record (every lane holds the same value)
-    uint32_t cnt;
-  };
   const int NC = a.max_rchunks + a.n_schunks;
   const __amdgpu_buffer_rsrc_t rch = make_rsrc(a.chunks, (uint32_t)NC * 16);
   const __amdgpu_buffer_rsrc_t rcn = make_rsrc(a.chunk_cnt, (uint32_t)NC * 4);
-  auto fetch = [&](int w, Item& it) {
+  // item w -> chunk, item within the chunk, routed (0) or shared (1)
+  auto locate = [&](int w, int& c, int& item, int& sh) {
     if (w < items_r) {
-      it.c = w / a.items[0];
-      it.item = w - it.c * a.items[0];
-      it.sh = 0;
+      c = w / a.items[0];
+      item = w - c * a.items[0];
+      sh = 0;
     } else {
       const int w2 = w - items_r;
       const int cs = w2 / a.items[1];
-      it.item = w2 - cs * a.items[1];
-      it.c = a.max_rchunks + cs;
-      it.sh = 1;
+      item = w2 - cs * a.items[1];
+      c = a.max_rchunks + cs;
+      sh = 1;
     }
-    it.ch = bld128(rch, 0u, (uint32_t)it.c * 16);
-    it.cnt = bld32(rcn, 0u, (uint32_t)it.c * 4);
   };
   const MatrixDev m0 = a.m[0], m1 = a.m[1];
+  const int w_beg = (int)(((long)items * xcd) >> 3);
   const int w_end = (int)(((long)items * (xcd + 1)) >> 3);
-  int w = (int)(((long)items * xcd) >> 3) + lw;
+  int w = w_beg + lw;
   if (w >= w_end) return;
-  Item it, nt;
-  fetch(w, it);
-  for (;; w += nlw) {
-    const bool more = w + nlw < w_end;
-    if (more) fetch(w + nlw, nt);
-    const MatrixDev M = it.sh ? m1 : m0;
-    const int ce = uniform((int)it.ch[0]), cs0 = uniform((int)it.ch[1]), cm = uniform((int)it.ch[2]);
-    const int cmask = uniform((int)it.ch[3]), ccnt = uniform((int)it.cnt);
-    switch (cmask & 15) {
+  NextVal cur;
+  {
+    int c, item, sh;
+    locate(w, c, item, sh);
+    const u32x4_t ch = bld128(rch, 0u, (uint32_t)c * 16);
+    cur.cnt = uniform((int)bld32(rcn, 0u, (uint32_t)c * 4));
+    cur.e = uniform((int)ch[0]);
+    cur.s0 = uniform((int)ch[1]);
+    cur.m = uniform((int)ch[2]);
+    cur.mask = uniform((int)ch[3]);
+  }
+  int nxt = w + nlw;
+  for (;;) {
+    int c, item, sh;
+    locate(w, c, item, sh);
+    const MatrixDev M = sh ? m1 : m0;
+    const bool more = nxt < w_end;
+    NextRec nr;
+    nr.ch = u32x4_t{0u, 0u, 0u, 0u};
+    nr.cnt = 0u;
+    if (more) {
+      int c2, i2, s2;
+      locate(nxt, c2, i2, s2);
+      nr.ch = bld128(rch, 0u, (uint32_t)c2 * 16);
+      nr.cnt = bld32(rcn, 0u, (uint32_t)c2 * 4);
+    }
+    NextVal nv;
+    switch (cur.mask & 15) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_item<MODE, QPK, MK>(a, M, it.c, ce, cs0, cm, ccnt, it.item); \
+    run_item<MODE, QPK, MK>(a, M, c, cur.e, cur.s0, cur.m, cur.cnt, item, nr, nv); \
     break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
       MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
 #undef MOE_CASE
       default:
+        nv.e = uniform((int)nr.ch[0]);
+        nv.s0 = uniform((int)nr.ch[1]);
+        nv.m = uniform((int)nr.ch[2]);
+        nv.mask = uniform((int)nr.ch[3]);
+        nv.cnt = uniform((int)nr.cnt);
         break;
     }
     if (!more) break;
-    it = nt;
+    w = nxt;
+    cur = nv;
+    nxt += nlw;
   }
 }
 
