@@ -7,6 +7,9 @@
 // (expert, token) dot products of its slice in float64 from exact bf16 /
 // fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
 // pair l, and wave 0 adds the eight slices in a fixed order.
+// Prefill-sized batches (T >= 256) take the logits on the fp64 matrix cores
+// instead: one wave per 16-token x 16-expert tile, v_mfma_f64_16x16x4f64 over
+// the hidden dimension (the same exact products, accumulated in fp64).
 // Top-k: one wave per token, k rounds of a wave-wide arg-max over (logit
 // desc, index asc) through DPP lane moves.
 #include "common.hpp"
@@ -114,6 +117,52 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_route_logits(const uint16_t* 
 
 }
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// One wave per 16 x 16 (token, expert) tile, four expert tiles per block.
+// Matrix-core operand layouts (16x16x4, fp64): lane l supplies A[l%16][l/16]
+// and B[l/16][l%16] and holds D[l/16 + 4r][l%16], r = 0..3 (rows interleaved,
+// unlike the fp32 16x16 layouts).  The hidden
+// dimension is walked in steps of 16 in which lane l owns columns
+// k0 + 4(l/16) + s, s = 0..3 (A and B share this order of k, which a sum does
+// not depend on): one 8-byte x load and one 16-byte W load per lane and step.
+__global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __restrict__ x, int T, int d,
+                                                           const float* __restrict__ W, int E,
+                                                           const float* __restrict__ bias,
+                                                           double* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.y * 16;
+  const int e0 = (blockIdx.x * 4 + wave) * 16;
+  if (e0 >= E) return;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int t = t0 + r16, e = e0 + r16;
+  const uint16_t* xr = x + (size_t)(t < T ? t : 0) * d + 4 * q;
+  const float* wr = W + (size_t)(e < E ? e : 0) * d + 4 * q;
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  uint2 xa = t < T ? *reinterpret_cast<const uint2*>(xr) : make_uint2(0u, 0u);
+  float4 wb = e < E ? *reinterpret_cast<const float4*>(wr) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < d; k0 += 16) {
+    const uint2 xc = xa;
+    const float4 wc = wb;
+    if (k0 + 16 < d) {
+      xa = t < T ? *reinterpret_cast<const uint2*>(xr + k0 + 16) : make_uint2(0u, 0u);
+      wb = e < E ? *reinterpret_cast<const float4*>(wr + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x & 0xFFFFu), (double)wc.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x >> 16), (double)wc.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y & 0xFFFFu), (double)wc.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y >> 16), (double)wc.w, acc, 0, 0, 0);
+  }
+  if (e < E) {
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = t0 + q + 4 * r;
+      if (tt < T) logits[(size_t)tt * E + e] = acc[r] + b;
+    }
+  }
+}
+
 }  // namespace
 
 size_t route_workspace_bytes(int T, int E) {
@@ -122,6 +171,11 @@ size_t route_workspace_bytes(int T, int E) {
 
 hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, int E, const float* bias,
                                double* logits, hipStream_t stream) {
+  if (T >= 256) {
+    dim3 grid((E + 63) / 64, (T + 15) / 16);
+    hipLaunchKernelGGL(k_route_logits_mfma, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
+    return hipGetLastError();
+  }
   dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
   hipLaunchKernelGGL(k_route_logits, grid, dim3(RT_WAVES * 64), 0, stream, x, T, d, W, E, bias, logits);
   return hipGetLastError();

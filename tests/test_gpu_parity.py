@@ -135,6 +135,21 @@ def test_route_ragged_token_counts(T):
     assert np.array_equal(idx.cpu().numpy()[ok], oidx[ok])
 
 
+@pytest.mark.parametrize("T", [256, 300, 1000])
+def test_route_matrix_core_logits_ragged(T):
+    # 256 tokens and more take the logits on the fp64 matrix cores (16-token
+    # tiles; 300 and 1000 leave a ragged last tile)
+    w, dev, _, _ = workload(4)
+    x = dev["x"][:T].contiguous()
+    note(f"route cfg4 T={T}")
+    idx, gate = bd.route(x, dev["w_router"], dev["bias"], w.cfg.k)
+    torch.cuda.synchronize()
+    oidx, ogate, gap, _ = orc.route(w.x_bf16[:T], w.w_router, w.logit_bias, w.cfg.k)
+    ok = gap >= TIE_GAP
+    assert np.array_equal(idx.cpu().numpy()[ok], oidx[ok])
+    assert np.allclose(gate.cpu().numpy()[ok], ogate[ok], rtol=4e-7, atol=1e-30)
+
+
 def test_route_exact_ties_go_to_lower_index():
     # duplicate router rows give exactly equal logits
     w, dev, _, _ = workload(1)
