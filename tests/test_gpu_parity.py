@@ -395,6 +395,28 @@ def test_ffn_qwen_decode_batch1():
     assert err < REL_L2, err
 
 
+# Small batches: one or a few pairs per expert, each chunk a single width
+# (T=1) or a few; the DeepSeek shape adds shared experts with an 11-k-block
+# down projection; group size 64 takes two-group k-blocks.
+@pytest.mark.parametrize("case", [(2, 1, {}), (2, 2, {}), (2, 4, {}), (2, 1, dict(g=64)), (3, 1, {}),
+                                  (3, 3, dict(b_lo=1))])
+def test_ffn_small_batches(case):
+    i, T, over = case
+    note(f"ffn small batch cfg{i} T={T} {over}")
+    err, _ = _ffn_case(i, T=T, over=over)
+    assert err < REL_L2, err
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ffn_small_batch_arbitrary_bit_mix(seed):
+    w, _, _, _ = workload(2)
+    rng = np.random.default_rng(20 + seed)
+    b = rng.integers(1, 5, size=4 * w.cfg.k)
+    note(f"ffn small batch cfg2 T=4 random bits seed={seed}")
+    err, _ = _ffn_case(2, bits_np=b, T=4)
+    assert err < REL_L2, err
+
+
 @pytest.mark.parametrize("b_lo", [1, 2])
 def test_ffn_deepseek_shared(b_lo):
     note(f"ffn cfg3 b_lo={b_lo}")
@@ -528,7 +550,8 @@ def test_stream_read_folds_every_word_once(nbytes):
 # the whole layer in one call: identical to route + alloc + FFN in sequence
 
 
-@pytest.mark.parametrize("case", [(1, {}), (1, dict(T=100)), (1, dict(T=300)), (2, dict(T=1)), (2, {}),
+@pytest.mark.parametrize("case", [(1, {}), (1, dict(T=100)), (1, dict(T=300)), (2, dict(T=1)), (2, dict(T=4)),
+                                  (3, dict(T=1)), (2, {}),
                                   (2, dict(T=128)), (3, {}), (3, dict(b_lo=1)), (4, dict(T=512))])
 def test_layer_call_equals_three_calls(case):
     i, over = case
