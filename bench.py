@@ -27,7 +27,13 @@ pairs); that line's roofline is matrix-core bound, in TFLOP/s of the
 routed experts' SwiGLU FFN (6 d f flops per routed pair) against the bf16
 dense peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--prefill]
+With --stack the step is a decode step through 48 such layers (T=64, each
+layer with its own router and expert bank, 16.3 GB resident): per layer
+the RMS-normalised bf16 cast of the fp32 residual as the layer's input,
+then one moe_layer call that adds its output into the residual; the
+targets 2.0 .. 4.0 in steps of 0.25 are swept.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--prefill | --stack]
 """
 from __future__ import annotations
 
@@ -265,6 +271,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20; 3 with --prefill)")
     ap.add_argument("--prefill", action="store_true",
                     help="the T=4096 Zipf-skewed prefill batch instead of the decode headline")
+    ap.add_argument("--stack", action="store_true",
+                    help="a decode step through the 48-layer stack (T=64) instead of the single-layer headline")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--target", type=float, default=3.0)
@@ -274,9 +282,9 @@ def main():
                          "size for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.steps is None:
-        args.steps = 20 if args.prefill else 200
+        args.steps = 20 if args.prefill else 48 if args.stack else 200
     if args.warmup is None:
-        args.warmup = 3 if args.prefill else 20
+        args.warmup = 3 if args.prefill else 8 if args.stack else 20
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer runs on a single MI355X and has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -300,6 +308,8 @@ def main():
 
     if args.prefill:
         return prefill(args, torch, bd, wl)
+    if args.stack:
+        return stack(args, torch, bd, wl)
     cfg = wl.config(2, T=args.tokens, target=args.target)
     log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
     t0 = time.perf_counter()
@@ -417,6 +427,147 @@ def prefill(args, torch, bd, wl):
                      "flops_per_launch": ev["ffn_flops"], "hbm_gbs": ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9,
                      "hbm_read_ceiling_gbs": ceiling},
         "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+N_LAYERS = 48
+RMS_EPS = 1e-6
+
+
+class Stack:
+    """The 48-layer stack on the device: per layer a router and an expert
+    bank; a fp32 residual h and its bf16 cast x; per layer the routing and
+    widths of the last step; HIP graphs of whole steps."""
+
+    def __init__(self, cfg, torch, bd, wl):
+        self.cfg, self.torch, self.bd = cfg, torch, bd
+        T, dev = cfg.T, "cuda"
+        self.layers = []
+        t0 = time.perf_counter()
+        for l in range(N_LAYERS):
+            wr, bank = wl.make_stack_layer(cfg, l)
+            self.layers.append((torch.from_numpy(wr).to(dev), bd.DeviceBank.from_host(bank)))
+            del wr, bank
+            if l % 8 == 7:
+                log(f"stack: {l + 1} layers resident ({time.perf_counter() - t0:.0f} s)")
+        self.h0 = [torch.from_numpy(wl.bf16_bits_to_f32(wl.step_activations(cfg, s, T))).to(dev)
+                   for s in range(N_XBATCH)]
+        self.h = torch.empty(T, cfg.d, dtype=torch.float32, device=dev)
+        self.x = torch.empty(T, cfg.d, dtype=torch.bfloat16, device=dev)
+        self.lws = bd.layer_workspace(self.layers[0][1], None, T, cfg.k)
+        self.idx = [torch.empty(T, cfg.k, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
+        self.gate = [torch.empty(T, cfg.k, dtype=torch.float32, device=dev) for _ in range(N_LAYERS)]
+        self.bits = [torch.empty(T * cfg.k, dtype=torch.uint8, device=dev) for _ in range(N_LAYERS)]
+        self.graphs = {}
+
+    def step(self, i, target):
+        """Decode step on activation batch i mod 8: h = x0, then per layer
+        h += layer(bf16(rmsnorm(h)))."""
+        bd, cfg = self.bd, self.cfg
+        self.h.copy_(self.h0[i % N_XBATCH])
+        bd.rmsnorm_to_bf16(self.h, self.x, eps=RMS_EPS)
+        for l, (wr, bank) in enumerate(self.layers):
+            bd.layer(bank, None, self.x, wr, None, cfg.k, cfg.b_lo, target, y=self.h, accumulate=True,
+                     idx=self.idx[l], gate=self.gate[l], bits=self.bits[l], workspace=self.lws)
+            bd.rmsnorm_to_bf16(self.h, self.x, eps=RMS_EPS)
+
+    def timed(self, target, steps, warmup):
+        """Steps replayed from a graph of one cycle of the 8 activation
+        batches (plus one of the remainder); seconds per step."""
+        torch = self.torch
+        key = float(target)
+        if key not in self.graphs:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.step(0, target)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            gs = []
+            for n in (N_XBATCH, steps % N_XBATCH):
+                if n == 0:
+                    gs.append(None)
+                    continue
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(n):
+                        self.step(i, target)
+                gs.append(g)
+            torch.cuda.synchronize()
+            self.graphs[key] = gs
+        full, rem = self.graphs[key]
+        for _ in range(max(1, -(-warmup // N_XBATCH))):
+            full.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps // N_XBATCH):
+            full.replay()
+        if rem is not None:
+            rem.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def step_bytes(self, target):
+        """Algorithmic bytes of one step (batch 0), from its routing and widths."""
+        self.step(0, target)
+        self.torch.cuda.synchronize()
+        tot, bread, balloc, nact = 0.0, [], [], []
+        for l in range(N_LAYERS):
+            b, br, ba, na = algorithmic_ffn_bytes(self.idx[l].cpu().numpy(), self.bits[l].cpu().numpy(), self.cfg,
+                                                  accumulate=True)
+            tot += b + router_bytes(self.cfg, self.cfg.T)
+            bread.append(br); balloc.append(ba); nact.append(na)
+        return tot, float(np.mean(bread)), float(np.mean(balloc)), float(np.mean(nact))
+
+
+def stack(args, torch, bd, wl):
+    cfg = wl.config(5, target=args.target)
+    T = cfg.T
+    log(f"generating the 48-layer Qwen3-30B-A3B-shaped stack, T={T} (seeded)")
+    S = Stack(cfg, torch, bd, wl)
+    targets = [args.target] if args.no_sweep else [2.0 + 0.25 * i for i in range(9)]
+    if args.target not in targets:
+        targets.insert(0, args.target)
+    sweep, head = [], None
+    for tgt in targets:
+        ts = S.timed(tgt, args.steps, args.warmup)
+        nbytes, br, ba, na = S.step_bytes(tgt)
+        row = dict(target=tgt, tokens_per_s=T / ts, ms_per_step=ts * 1e3, step_gbs=nbytes / ts / 1e9,
+                   step_bytes=nbytes, bits_read=br, bits_alloc=ba, n_active=na)
+        sweep.append(row)
+        log(f"stack target={tgt}: {T / ts:.0f} tok/s, {ts * 1e3:.3f} ms per step, {nbytes / ts / 1e9:.0f} GB/s, "
+            f"bits read {br:.2f}, bits allocated {ba:.2f}")
+        if tgt == args.target:
+            head = (ts, row)
+    ceiling = read_ceiling(torch, bd)
+    ts, row = head
+    out = {
+        "metric": "48-layer stack decode tokens/s + achieved HBM GB/s vs avg bits read (Qwen3-30B shape)",
+        "value": T / ts,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ts * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "48 Qwen3-30B-A3B-shaped MoE layers, decode, residual carried", "tokens": T,
+                   "layers": N_LAYERS, "hidden": cfg.d, "expert_intermediate": cfg.f, "experts": cfg.E,
+                   "top_k": cfg.k, "bitplanes": cfg.b_max, "group": cfg.g, "b_lo": cfg.b_lo,
+                   "target_avg_bits": args.target, "activation_batches": N_XBATCH},
+        "bits_read": row["bits_read"],
+        "bits_alloc": row["bits_alloc"],
+        "n_active_experts": row["n_active"],
+        "roofline": {"bound": "hbm", "achieved": row["step_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": row["step_gbs"] / HBM_PEAK_GBS, "traffic": None, "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": row["step_gbs"] / ceiling,
+                     "kernel": "whole step: 48 x (RMS-normalised cast + moe_layer)", "bytes_per_step": row["step_bytes"]},
+        "cpu_baseline": None,
+        "sweep": sweep,
     }
     print(json.dumps(out), flush=True)
 

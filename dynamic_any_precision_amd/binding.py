@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer": (i32, [bp, bp, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp, sz, vp]),
             "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
+            "moe_rmsnorm_to_bf16": (i32, [vp, vp, i32, i32, f32, vp]),
             "moe_stream_read": (i32, [vp, i64, vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
@@ -296,6 +297,18 @@ def residual_to_bf16(h: torch.Tensor, x: Optional[torch.Tensor] = None, stream=N
         x = torch.empty(h.shape, dtype=torch.bfloat16, device=h.device)
     st = lib().moe_residual_to_bf16(_ptr(h, torch.float32, "h"), _ptr(x, _BF16, "x"), h.numel(), _stream(stream))
     _check(st, "moe_residual_to_bf16")
+    return x
+
+
+def rmsnorm_to_bf16(h: torch.Tensor, x: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                    stream=None) -> torch.Tensor:
+    """Rows of h [T][d] fp32 scaled to unit root-mean-square, as bf16."""
+    rows, d = h.shape
+    if x is None:
+        x = torch.empty(h.shape, dtype=torch.bfloat16, device=h.device)
+    st = lib().moe_rmsnorm_to_bf16(_ptr(h, torch.float32, "h"), _ptr(x, _BF16, "x"), rows, d, float(eps),
+                                   _stream(stream))
+    _check(st, "moe_rmsnorm_to_bf16")
     return x
 
 

@@ -290,6 +290,13 @@ moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* st
   return hip_status(moe::launch_residual_to_bf16(h, x, n, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_rmsnorm_to_bf16(const float* h, uint16_t* x, int32_t rows, int32_t d, float eps, void* stream) {
+  if (rows < 0 || d < 1 || !(eps >= 0.0f) || eps > 3.0e38f) return MOE_ERR_RANGE;
+  if (rows == 0) return MOE_OK;
+  if (!h || !x) return MOE_ERR_NULL;
+  return hip_status(moe::launch_rmsnorm_to_bf16(h, x, rows, d, eps, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (bytes < 0 || bytes % 16) return MOE_ERR_RANGE;
   if (bytes == 0) return MOE_OK;

@@ -1,5 +1,6 @@
 // Floor-and-compensation dequantisation of one stored matrix (MatMoE review,
-// Core Contribution, F&C paragraph), and the bf16 cast of a residual stream.
+// Core Contribution, F&C paragraph), and the bf16 layer input of a residual
+// stream (plain cast, or RMS-normalised rows).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,6 +37,27 @@ __global__ __launch_bounds__(256) void k_residual_to_bf16(const float* __restric
                                                           int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) x[i] = (uint16_t)f32_to_bf16(h[i]);
+}
+
+// One block per row of d values: r = fp32(1 / sqrt(sum(h^2) / d + eps)) with
+// the squares and their sum in fp64 (each square exact; the sum's order
+// moves only its last fp64 bits), then x = bf16_rne(fp32(h * r)).
+__global__ __launch_bounds__(256) void k_rmsnorm_to_bf16(const float* __restrict__ h, uint16_t* __restrict__ x,
+                                                         int d, float eps) {
+  __shared__ double part[4];
+  const float* hr = h + (size_t)blockIdx.x * d;
+  uint16_t* xr = x + (size_t)blockIdx.x * d;
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const double v = (double)hr[i];
+    ss = fma(v, v, ss);
+  }
+  ss = wave_sum_d(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const double tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = (float)(1.0 / sqrt(tot / (double)d + (double)eps));
+  for (int i = threadIdx.x; i < d; i += 256) xr[i] = (uint16_t)f32_to_bf16(__fmul_rn(hr[i], r));
 }
 
 // Streaming read: blocks of 256 threads, 8 loads of 16 B in flight per thread
@@ -78,6 +100,12 @@ hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(256), 0, stream, m.planes, m.sz, m.N, m.K, B, g, expert, bits,
                      out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_to_bf16(const float* h, uint16_t* x, int rows, int d, float eps, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_to_bf16, dim3(rows), dim3(256), 0, stream, h, x, d, eps);
   return hipGetLastError();
 }
 

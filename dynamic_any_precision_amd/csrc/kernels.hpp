@@ -73,6 +73,7 @@ hipError_t launch_combine(const FfnShape& s, const FfnLayout& L, char* ws, const
 // ---- helpers
 hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream);
 hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream);
+hipError_t launch_rmsnorm_to_bf16(const float* h, uint16_t* x, int rows, int d, float eps, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int sink_len, hipStream_t stream);
 
 }  // namespace moe

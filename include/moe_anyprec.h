@@ -254,6 +254,20 @@ moe_status moe_dequant(const moe_expert_bank* bank, int32_t expert, int32_t matr
 moe_status moe_residual_to_bf16(const float* h, uint16_t* x, int64_t n, void* stream);
 
 /*
+ * The next layer's input from an fp32 residual stream with each row
+ * RMS-normalised, as the Qwen3-MoE-shaped stacks do before every MoE layer
+ * (the pages define the layer, not the stack around it; this is the reading
+ * taken for a 48-layer stack, whose un-normalised residual overflows fp32
+ * within a few SwiGLU layers):
+ *   r = fp32(1 / sqrt(sum_c h[t][c]^2 / d + eps))   (squares and sum in fp64)
+ *   x[t][c] = bf16_round_nearest_even(fp32(h[t][c] * r))
+ * h [rows][d] fp32, x [rows][d] bf16 bits, both device, row-major, not
+ * overlapping.  rows >= 0, d >= 1, 0 <= eps finite; otherwise MOE_ERR_RANGE.
+ * A row of zeros needs eps > 0 (with eps = 0 its scale is infinite).
+ */
+moe_status moe_rmsnorm_to_bf16(const float* h, uint16_t* x, int32_t rows, int32_t d, float eps, void* stream);
+
+/*
  * Measurement helper, for callers that compare a kernel's rate with what the
  * memory system can deliver: a pure streaming read of `bytes` bytes of `buf`
  * (16-byte loads, every byte read once, nothing else moved), the achievable

@@ -235,6 +235,23 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return np.ldexp(np.round(m * 256.0), e - 8)
 
 
+def rmsnorm_bf16(h: np.ndarray, eps: float) -> np.ndarray:
+    """Layer input of the residual stack from the fp32 residual h [T][d]:
+    each row scaled by r = fp32(1 / sqrt(mean of its squares + eps)), the
+    product rounded to fp32, then to bf16 (returned as float64 values).
+
+    Not from the pages: they define one MoE layer, not a stack.  Reading: a
+    48-layer stack of these SwiGLU layers carries its residual through a
+    root-mean-square normalisation before each layer, as the Qwen3-MoE
+    models the stack is shaped after do (unit weight, eps 1e-6); without it
+    the residual overflows fp32 within a few layers.  The mean of squares is
+    taken in float64 (each square of an fp32 value is exact there)."""
+    h = np.asarray(h, dtype=np.float32)
+    ms = np.sum(h.astype(np.float64) ** 2, axis=-1) / h.shape[-1] + float(eps)
+    r = (1.0 / np.sqrt(ms)).astype(np.float32)
+    return round_bf16((h * r[..., None]).astype(np.float32))
+
+
 def silu(v: np.ndarray) -> np.ndarray:
     return v / (1.0 + np.exp(-v))
 

@@ -122,6 +122,13 @@ def test_other_entry_points_validate(L):
     assert L.moe_residual_to_bf16(None, None, 0, None) == OK
     assert L.moe_residual_to_bf16(None, fake, 4, None) == NULL
     assert L.moe_residual_to_bf16(fake, fake, -1, None) == RANGE
+    assert L.moe_rmsnorm_to_bf16(None, None, 0, 2048, 1e-6, None) == OK
+    assert L.moe_rmsnorm_to_bf16(None, fake, 4, 2048, 1e-6, None) == NULL
+    assert L.moe_rmsnorm_to_bf16(fake, fake, -1, 2048, 1e-6, None) == RANGE
+    assert L.moe_rmsnorm_to_bf16(fake, fake, 4, 0, 1e-6, None) == RANGE
+    assert L.moe_rmsnorm_to_bf16(fake, fake, 4, 2048, -1.0, None) == RANGE
+    assert L.moe_rmsnorm_to_bf16(fake, fake, 4, 2048, float("nan"), None) == RANGE
+    assert L.moe_rmsnorm_to_bf16(fake, fake, 4, 2048, float("inf"), None) == RANGE
 
 
 def test_stream_read_validation(L):

@@ -474,14 +474,21 @@ def test_ffn_wide_chunks_deepseek_shared():
     assert err < REL_L2, err
 
 
+def _check_rmsnorm(h, x, eps):
+    ref = orc.rmsnorm_bf16(h.cpu().numpy(), eps)
+    assert np.array_equal(x.float().cpu().numpy().astype(np.float64), ref)
+
+
 def test_stack_layers_teacher_forced():
     # three layers of the 48-layer stack shape, T=64: the residual is carried
-    # on the GPU (fp32 h, bf16 layer input); each layer's output is checked
-    # against the oracle on the GPU's own layer input (teacher forcing)
+    # on the GPU (fp32 h, RMS-normalised bf16 layer input, checked bit for
+    # bit); each layer's output is checked against the oracle on the GPU's
+    # own layer input (teacher forcing)
     cfg = wl.config(5)
     rng = np.random.default_rng(5)
     h = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)).cuda()
-    x = bd.residual_to_bf16(h)
+    x = bd.rmsnorm_to_bf16(h, eps=1e-6)
+    _check_rmsnorm(h, x, 1e-6)
     rows = [0, 17, 63]
     for layer in range(3):
         w_router, bank = wl.make_stack_layer(cfg, layer)
@@ -498,7 +505,8 @@ def test_stack_layers_teacher_forced():
                           bits.cpu().numpy(), oc, tokens=rows)
         got = h.cpu().numpy().astype(np.float64)[rows] - y0.cpu().numpy().astype(np.float64)[rows]
         assert rel_l2(got, ref[rows]) < REL_L2, layer
-        x = bd.residual_to_bf16(h)
+        x = bd.rmsnorm_to_bf16(h, eps=1e-6)
+        _check_rmsnorm(h, x, 1e-6)
         del dev_bank
 
 
@@ -518,6 +526,21 @@ def test_ffn_drops_invalid_pairs():
     ii = idx.cpu().numpy()
     ref = orc.combine(w.x_bf16, ii, g, bits.cpu().numpy(), oc)
     assert rel_l2(y.cpu().numpy(), ref) < REL_L2
+
+
+@pytest.mark.parametrize("rows,d", [(64, 2048), (3, 100), (5, 1), (1, 4096)])
+def test_rmsnorm_to_bf16_exact(rows, d):
+    # rows of very different magnitudes, a zero row, ragged widths
+    rng = np.random.default_rng(rows * 1000 + d)
+    h = (rng.standard_normal((rows, d)) * 10.0 ** rng.integers(-4, 5, (rows, 1))).astype(np.float32)
+    if rows > 2:
+        h[1] = 0.0
+    note(f"rmsnorm_to_bf16 rows={rows} d={d}")
+    ht = torch.from_numpy(h).cuda()
+    for eps in (1e-6, 0.5):
+        x = bd.rmsnorm_to_bf16(ht, eps=eps)
+        torch.cuda.synchronize()
+        _check_rmsnorm(ht, x, eps)
 
 
 def test_residual_to_bf16_exact():

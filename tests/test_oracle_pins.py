@@ -299,6 +299,47 @@ def test_round_bf16_matches_torch():
     assert np.array_equal(orc.round_bf16(v.astype(np.float64)), ref)
 
 
+# ---------------------------------------------------------------------------
+# stack: RMS-normalised bf16 layer input (a reading, not from the pages)
+
+
+def test_rmsnorm_worked_example():
+    # h = (3, 4), eps = 0: mean square 12.5, r = 0.28284271...;
+    # 3r = 0.848528 = 1.697056 * 2^-1, whose 8-bit significand 217.22/128
+    # rounds to 217/128: 0.84765625;  4r = 1.131371 = 144.816/128 -> 145/128
+    got = orc.rmsnorm_bf16(np.array([[3.0, 4.0]], dtype=np.float32), 0.0)
+    assert got.tolist() == [[0.84765625, 1.1328125]]
+
+
+def test_rmsnorm_constant_rows_are_plus_minus_one():
+    # a row of one value c has root-mean-square |c|: every output is sign(c)
+    for c in (3.7, -0.011, 1234.5):
+        got = orc.rmsnorm_bf16(np.full((1, 1024), c, dtype=np.float32), 0.0)
+        assert np.all(got == np.sign(c)), c
+
+
+def test_rmsnorm_power_of_two_scale_invariance():
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((8, 2048)).astype(np.float32)
+    base = orc.rmsnorm_bf16(h, 0.0)
+    for k in (-20, -3, 5, 30):
+        assert np.array_equal(orc.rmsnorm_bf16(h * np.float32(2.0 ** k), 0.0), base), k
+
+
+def test_rmsnorm_unit_mean_square_and_eps():
+    rng = np.random.default_rng(12)
+    h = (rng.standard_normal((16, 2048)) * 10.0 ** rng.integers(-2, 3, (16, 1))).astype(np.float32)
+    x = orc.rmsnorm_bf16(h, 1e-6)
+    # mean square of the output: m / (m + eps) for a row of mean square m
+    m = np.mean(h.astype(np.float64) ** 2, axis=1)
+    assert np.allclose(np.mean(x * x, axis=1), m / (m + 1e-6), atol=4e-3)
+    assert np.all(np.sign(x) == np.sign(h))
+    # eps dominates a tiny row: x = h / sqrt(h^2 + eps) for a constant row
+    tiny = orc.rmsnorm_bf16(np.full((1, 64), 1e-5, dtype=np.float32), 1e-6)
+    assert np.allclose(tiny, 1e-5 / math.sqrt(1e-10 + 1e-6), rtol=2 ** -8)
+    assert np.all(orc.rmsnorm_bf16(np.zeros((2, 64), dtype=np.float32), 1e-6) == 0.0)
+
+
 def _bit_of(planes_e_p, N, K, n, c):
     """Read one stored bit by walking the layout definition step by step."""
     tile, r = divmod(n, 16)
