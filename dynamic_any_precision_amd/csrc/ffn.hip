@@ -219,8 +219,11 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   const int c = blockIdx.x;  // 16-token block: chunk c / sub, block c % sub of it
   const int kb = blockIdx.y;
   const int ck = c / a.sub;
-  if (ck < a.max_rchunks && ck >= a.meta[0]) return;
+  // the chunk record is loaded with the routed chunk count, not after it
+  // (every record index is inside the chunk array)
+  const int nrc = a.meta[0];
   const int4 ch = a.chunks[ck];
+  if (ck < a.max_rchunks && ck >= nrc) return;
   const int s0 = ch.y + 16 * (c - ck * a.sub), m = ch.z - 16 * (c - ck * a.sub);
   const int tid = threadIdx.x, t = tid >> 4, q = tid & 15;
   __shared__ uint4 frag[256];
@@ -1049,6 +1052,11 @@ __global__ __launch_bounds__(256) void k_hsum(const FfnArgs a, int nblocks, int 
 // ---------------------------------------------------------------------------
 // combine: y[t] = (acc ? y[t] : 0) + sum_j gate[t][j] o_(t,j) + sum_s o_(t,shared s)
 
+// top_k <= 8 (checked at the boundary): all slots and gates are loaded
+// first, then all rows, then added in pair order, so the loads take one
+// round trip each instead of one per pair.
+constexpr int CMB_KMAX = 8;
+
 __global__ __launch_bounds__(256) void k_combine(int T, int k, int d, int P, int n_shared,
                                                  const int* __restrict__ pair_slot, const float* __restrict__ gate,
                                                  const float* __restrict__ obuf, float* __restrict__ y,
@@ -1057,12 +1065,21 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int d, int P, int
   const int n4 = blockIdx.x * blockDim.x + threadIdx.x;
   if (n4 * 4 >= d) return;
   float4 v = accumulate ? reinterpret_cast<const float4*>(y + (size_t)t * d)[n4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int s = pair_slot[t * k + j];
-    if (s < 0) continue;
-    const float gt = gate[t * k + j];
-    const float4 o = reinterpret_cast<const float4*>(obuf + (size_t)s * d)[n4];
-    v.x += gt * o.x; v.y += gt * o.y; v.z += gt * o.z; v.w += gt * o.w;
+  int sl[CMB_KMAX];
+  float gt[CMB_KMAX];
+#pragma unroll
+  for (int j = 0; j < CMB_KMAX; ++j) {
+    sl[j] = j < k ? pair_slot[t * k + j] : -1;
+    gt[j] = j < k ? gate[t * k + j] : 0.f;
+  }
+  float4 o[CMB_KMAX];
+#pragma unroll
+  for (int j = 0; j < CMB_KMAX; ++j)
+    o[j] = sl[j] >= 0 ? reinterpret_cast<const float4*>(obuf + (size_t)sl[j] * d)[n4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < CMB_KMAX; ++j) {
+    if (sl[j] < 0) continue;
+    v.x += gt[j] * o[j].x; v.y += gt[j] * o[j].y; v.z += gt[j] * o[j].z; v.w += gt[j] * o[j].w;
   }
   for (int sh = 0; sh < n_shared; ++sh) {
     const float4 o = reinterpret_cast<const float4*>(obuf + (size_t)(P + sh * T + t) * d)[n4];
@@ -1188,9 +1205,11 @@ hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, Matrix
 hipError_t launch_combine(const FfnShape& s, const FfnLayout& L, char* ws, const float* gate, float* y,
                           int accumulate, hipStream_t stream) {
   dim3 grid((s.d / 4 + 255) / 256, s.T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, s.T, s.k, s.d, s.P, s.n_shared,
-                     reinterpret_cast<const int*>(ws + L.pair_slot), gate,
-                     reinterpret_cast<const float*>(ws + L.obuf), y, accumulate);
+  const int* ps = reinterpret_cast<const int*>(ws + L.pair_slot);
+  const float* ob = reinterpret_cast<const float*>(ws + L.obuf);
+  if (s.k > CMB_KMAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, s.T, s.k, s.d, s.P, s.n_shared, ps, gate, ob, y,
+                     accumulate);
   return hipGetLastError();
 }
 
