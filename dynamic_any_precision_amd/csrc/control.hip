@@ -109,20 +109,32 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
   __syncthreads();
 
   // allocation: high width iff #{keys >= own key} <= n*; the keys past P
-  // (up to a multiple of 8) read as 0, below every gate key
+  // (up to a multiple of 8) read as 0, below every gate key.  Up to 256
+  // pairs, four adjacent threads split a pair's count over the key blocks.
   for (int j = s.P + tid; j < ((s.P + 7) & ~7); j += PM_NT) skey[j] = 0u;
   __syncthreads();
-  if (tid < s.P) {
-    const uint32_t v = skey[tid];
+  {
+    const int tpp = s.P <= PM_NT / 4 ? 4 : 1;  // threads per pair
+    const int i = tid / tpp, part = tid % tpp;
+    const int nblk = (s.P + 7) / 8;
     int ge = 0;
-    const uint4* k4 = reinterpret_cast<const uint4*>(skey);
-    for (int j = 0; j < (s.P + 7) / 8; ++j) {
-      const uint4 a = k4[2 * j], b = k4[2 * j + 1];
-      ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
+    if (i < s.P) {
+      const uint32_t v = skey[i];
+      const uint4* k4 = reinterpret_cast<const uint4*>(skey);
+      for (int j = part * nblk / tpp; j < (part + 1) * nblk / tpp; ++j) {
+        const uint4 a = k4[2 * j], b = k4[2 * j + 1];
+        ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
+      }
     }
-    const int b = ge <= n_star ? b_max : b_lo;
-    bits_out[tid] = (uint8_t)b;
-    L.sbits[tid] = (uint8_t)b;
+    if (tpp == 4) {  // uniform over the block
+      ge += __shfl_xor(ge, 1, WAVE);
+      ge += __shfl_xor(ge, 2, WAVE);
+    }
+    if (i < s.P && part == 0) {
+      const int b = ge <= n_star ? b_max : b_lo;
+      bits_out[i] = (uint8_t)b;
+      L.sbits[i] = (uint8_t)b;
+    }
   }
   __syncthreads();
 
