@@ -389,6 +389,13 @@ def test_ffn_qwen_decode(target):
     assert err < REL_L2, err
 
 
+def test_ffn_qwen_decode_group64():
+    # two quant groups per k-block on the decode path with many items
+    note("ffn cfg2 T=32 g=64")
+    err, _ = _ffn_case(2, tokens=[0, 7, 19, 31], over=dict(g=64))
+    assert err < REL_L2, err
+
+
 def test_ffn_qwen_decode_batch1():
     note("ffn cfg2 T=1")
     err, _ = _ffn_case(2, T=1, target=3.0)
