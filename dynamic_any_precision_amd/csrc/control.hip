@@ -110,11 +110,12 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
 
   // allocation: high width iff #{keys >= own key} <= n*; the keys past P
   // (up to a multiple of 8) read as 0, below every gate key.  Up to 256
-  // pairs, four adjacent threads split a pair's count over the key blocks.
+  // (512) pairs, four (two) adjacent threads split a pair's count over the
+  // key blocks.
   for (int j = s.P + tid; j < ((s.P + 7) & ~7); j += PM_NT) skey[j] = 0u;
   __syncthreads();
   {
-    const int tpp = s.P <= PM_NT / 4 ? 4 : 1;  // threads per pair
+    const int tpp = s.P <= PM_NT / 4 ? 4 : s.P <= PM_NT / 2 ? 2 : 1;  // threads per pair
     const int i = tid / tpp, part = tid % tpp;
     const int nblk = (s.P + 7) / 8;
     int ge = 0;
@@ -126,10 +127,8 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
         ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
       }
     }
-    if (tpp == 4) {  // uniform over the block
-      ge += __shfl_xor(ge, 1, WAVE);
-      ge += __shfl_xor(ge, 2, WAVE);
-    }
+    if (tpp >= 2) ge += __shfl_xor(ge, 1, WAVE);  // tpp is uniform over the block
+    if (tpp == 4) ge += __shfl_xor(ge, 2, WAVE);
     if (i < s.P && part == 0) {
       const int b = ge <= n_star ? b_max : b_lo;
       bits_out[i] = (uint8_t)b;

@@ -580,7 +580,8 @@ def test_stream_read_folds_every_word_once(nbytes):
 # the whole layer in one call: identical to route + alloc + FFN in sequence
 
 
-@pytest.mark.parametrize("case", [(1, {}), (1, dict(T=100)), (1, dict(T=300)), (2, dict(T=1)), (2, dict(T=4)),
+@pytest.mark.parametrize("case", [(1, {}), (1, dict(T=100)), (1, dict(T=200)), (1, dict(T=300)), (2, dict(T=1)),
+                                  (2, dict(T=4)), (2, dict(T=64)),
                                   (3, dict(T=1)), (2, {}),
                                   (2, dict(T=128)), (3, {}), (3, dict(b_lo=1)), (4, dict(T=512))])
 def test_layer_call_equals_three_calls(case):
