@@ -27,13 +27,19 @@ pairs); that line's roofline is matrix-core bound, in TFLOP/s of the
 routed experts' SwiGLU FFN (6 d f flops per routed pair) against the bf16
 dense peak.
 
+With --calibrated the widths come from a gate threshold calibrated once
+(MatMoE's calibration-threshold mode): the bisection runs over the gates of
+64 calibration batches, and each step then runs the router, the fixed-
+threshold widths and the FFN; the line reports the spread of the per-step
+average width over 64 held-out batches for targets 2.5, 3.0 and 3.5.
+
 With --stack the step is a decode step through 48 such layers (T=64, each
 layer with its own router and expert bank, 16.3 GB resident): per layer
 the RMS-normalised bf16 cast of the fp32 residual as the layer's input,
 then one moe_layer call that adds its output into the residual; the
 targets 2.0 .. 4.0 in steps of 0.25 are swept.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--prefill | --stack]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--prefill | --stack | --calibrated]
 """
 from __future__ import annotations
 
@@ -149,6 +155,7 @@ class Layer:
         self.bits = [torch.empty(T * cfg.k, dtype=torch.uint8, device=dev) for _ in range(N_XBATCH)]
         self.y = torch.empty(T, cfg.d, dtype=torch.float32, device=dev)
         self.graphs = {}
+        self.tau = None  # calibration-threshold mode: fixed gate threshold (host float)
 
     def step(self, i, target, ev=None):
         """One layer step: moe_layer (one call), or with ev the three calls
@@ -156,6 +163,17 @@ class Layer:
         bd, cfg = self.bd, self.cfg
         s = i % N_XBATCH
         bank = self.banks[i % N_COPIES]
+        if self.tau is not None:
+            # calibration-threshold mode: route, fixed-threshold widths, FFN
+            bd.route(self.xs[s], self.wr, self.bias, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
+            bd.bits_from_threshold(self.gate[s].view(-1), self.tau, cfg.b_lo, cfg.b_max, bits=self.bits[s])
+            if ev is not None:
+                ev[0].record()
+            bd.anyprec_ffn(bank, None, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
+                           workspace=self.fws)
+            if ev is not None:
+                ev[1].record()
+            return
         if ev is None:
             bd.layer(bank, None, self.xs[s], self.wr, self.bias, cfg.k, cfg.b_lo, target, y=self.y, idx=self.idx[s],
                      gate=self.gate[s], bits=self.bits[s], workspace=self.lws)
@@ -273,6 +291,8 @@ def main():
                     help="the T=4096 Zipf-skewed prefill batch instead of the decode headline")
     ap.add_argument("--stack", action="store_true",
                     help="a decode step through the 48-layer stack (T=64) instead of the single-layer headline")
+    ap.add_argument("--calibrated", action="store_true",
+                    help="calibration-threshold mode: a gate threshold fixed from calibration batches")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--target", type=float, default=3.0)
@@ -310,6 +330,8 @@ def main():
         return prefill(args, torch, bd, wl)
     if args.stack:
         return stack(args, torch, bd, wl)
+    if args.calibrated:
+        return calibrated(args, torch, bd, wl)
     cfg = wl.config(2, T=args.tokens, target=args.target)
     log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
     t0 = time.perf_counter()
@@ -427,6 +449,76 @@ def prefill(args, torch, bd, wl):
                      "flops_per_launch": ev["ffn_flops"], "hbm_gbs": ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9,
                      "hbm_read_ceiling_gbs": ceiling},
         "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+N_CAL = 64  # calibration batches (and as many held-out batches)
+
+
+def calibrated(args, torch, bd, wl):
+    cfg = wl.config(2, T=args.tokens, target=args.target)
+    T = cfg.T
+    log(f"generating the Qwen3-30B-A3B-shaped layer (seeded); calibration-threshold mode, T={T}")
+    w = wl.make_workload(cfg, keep_codes=False)
+    L = Layer(cfg, w, torch, bd, T)
+
+    def gates_of(first):
+        out = []
+        for s in range(N_CAL):
+            x = bd.bf16_tensor(wl.step_activations(cfg, first + s, T))
+            out.append(bd.route(x, L.wr, L.bias, cfg.k)[1].reshape(-1))
+        return torch.cat(out)
+
+    cal, held = gates_of(10_000), gates_of(20_000)   # distinct from the timed batches (steps 0..7)
+    tau_t = torch.empty(1, dtype=torch.float32, device="cuda")
+    rows, head = [], None
+    for tgt in sorted({2.5, 3.0, 3.5, args.target}):
+        bd.alloc_bits(cal, cfg.b_lo, cfg.b_max, tgt, tau=tau_t)   # the bisection, once, on the calibration set
+        tau = float(tau_t.item())
+        hb = bd.bits_from_threshold(held, tau, cfg.b_lo, cfg.b_max).view(N_CAL, T * cfg.k).float().mean(1).cpu().numpy()
+        L.tau = tau
+        ts = L.timed_graph(tgt, args.steps, args.warmup)
+        ev = L.timed_events(tgt, args.steps)
+        row = dict(target=tgt, tau=tau, tokens_per_s=T / ts, ms_per_step=ts * 1e3, ffn_ms=ev["ffn_ms"],
+                   ffn_gbs=ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9, bits_read=ev["bits_read"],
+                   held_out_bits={"mean": float(hb.mean()), "std": float(hb.std()), "min": float(hb.min()),
+                                  "max": float(hb.max())})
+        rows.append(row)
+        log(f"calibrated target={tgt}: tau {tau:.6g}, {T / ts:.0f} tok/s, FFN {ev['ffn_ms'] * 1e3:.1f} us; held-out "
+            f"per-step bits {hb.mean():.3f} +- {hb.std():.3f} (min {hb.min():.3f}, max {hb.max():.3f})")
+        if tgt == args.target:
+            head = (ts, ev, row)
+    ts, ev, row = head
+    achieved = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "MoE-layer tokens/s, calibration-threshold mode (Qwen3-30B shape)",
+        "value": T / ts,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ts * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer, decode, calibrated gate threshold",
+                   "tokens": T, "hidden": cfg.d, "expert_intermediate": cfg.f, "experts": cfg.E, "top_k": cfg.k,
+                   "bitplanes": cfg.b_max, "group": cfg.g, "b_lo": cfg.b_lo, "target_avg_bits": args.target,
+                   "calibration_batches": N_CAL, "held_out_batches": N_CAL,
+                   "weight_copies_rotated": N_COPIES, "activation_batches": N_XBATCH},
+        "tau": row["tau"],
+        "held_out_bits": row["held_out_bits"],
+        "bits_read": ev["bits_read"],
+        "bits_alloc": ev["bits_alloc"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
+                     "bytes_per_launch": ev["ffn_bytes"]},
+        "cpu_baseline": None,
+        "sweep": rows,
     }
     print(json.dumps(out), flush=True)
 

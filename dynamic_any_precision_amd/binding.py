@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
             "moe_rmsnorm_to_bf16": (i32, [vp, vp, i32, i32, f32, vp]),
+            "moe_bits_from_threshold": (i32, [vp, i32, f32, i32, i32, vp, vp]),
             "moe_stream_read": (i32, [vp, i64, vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
@@ -205,6 +206,18 @@ def alloc_bits(gate: torch.Tensor, b_lo: int, b_max: int, target: float, bits: O
                               _ptr(bits, torch.uint8, "bits"), _ptr(tau, torch.float32, "tau"),
                               _ptr(n_hi, torch.int32, "n_hi"), _stream(stream))
     _check(st, "moe_alloc_bits")
+    return bits
+
+
+def bits_from_threshold(gate: torch.Tensor, tau: float, b_lo: int, b_max: int,
+                        bits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Widths from a fixed gate threshold (calibration-threshold mode)."""
+    P = gate.numel()
+    if bits is None:
+        bits = torch.empty(P, dtype=torch.uint8, device=gate.device)
+    st = lib().moe_bits_from_threshold(_ptr(gate, torch.float32, "gate"), P, float(tau), b_lo, b_max,
+                                       _ptr(bits, torch.uint8, "bits"), _stream(stream))
+    _check(st, "moe_bits_from_threshold")
     return bits
 
 

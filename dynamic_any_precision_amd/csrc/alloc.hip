@@ -1,7 +1,9 @@
 // Bit allocation by threshold bisection (MatMoE abstract item (3) and review,
 // Core Contribution: a routing-score threshold found by binary search so the
 // batch meets a target average bit-width; DPA-MoE abstract: allocation after
-// routing from live gate scores).
+// routing from live gate scores), and the widths from a fixed threshold
+// (the same review: the threshold set on a calibration distribution of
+// routing scores and then applied as is).
 //
 // One block (one wave when P <= 2048).  Gate scores are mapped to
 // order-preserving 32-bit keys and held in registers; tau is built from its
@@ -86,7 +88,20 @@ __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, in
   }
 }
 
+// Fixed-threshold widths (calibration-threshold mode): one thread per pair.
+__global__ __launch_bounds__(256) void k_bits_threshold(const float* __restrict__ gate, int P, float tau, int b_lo,
+                                                        int b_max, uint8_t* __restrict__ bits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < P) bits[i] = (uint8_t)(gate[i] > tau ? b_max : b_lo);
+}
+
 }  // namespace
+
+hipError_t launch_bits_threshold(const float* gate, int P, float tau, int b_lo, int b_max, uint8_t* bits,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(k_bits_threshold, dim3((P + 255) / 256), dim3(256), 0, stream, gate, P, tau, b_lo, b_max, bits);
+  return hipGetLastError();
+}
 
 hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_max, uint8_t* bits, float* tau_out,
                         int* n_hi_out, hipStream_t stream) {

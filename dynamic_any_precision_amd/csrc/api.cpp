@@ -176,6 +176,14 @@ moe_status moe_alloc_bits(const float* gate, int32_t P, int32_t b_lo, int32_t b_
                                       static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_bits_from_threshold(const float* gate, int32_t P, float tau, int32_t b_lo, int32_t b_max,
+                                   uint8_t* bits, void* stream) {
+  if (P < 0 || b_lo < 1 || b_max > 4 || b_lo > b_max || tau != tau) return MOE_ERR_RANGE;
+  if (P == 0) return MOE_OK;
+  if (!gate || !bits) return MOE_ERR_NULL;
+  return hip_status(moe::launch_bits_threshold(gate, P, tau, b_lo, b_max, bits, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_ffn_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T,
                                int32_t top_k) {
   moe::FfnShape s;

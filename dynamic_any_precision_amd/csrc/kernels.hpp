@@ -19,6 +19,8 @@ hipError_t launch_route_topk(const double* logits, int T, int E, int k, int reno
 // ---- allocation
 hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_max, uint8_t* bits, float* tau_out,
                         int* n_hi_out, hipStream_t stream);
+hipError_t launch_bits_threshold(const float* gate, int P, float tau, int b_lo, int b_max, uint8_t* bits,
+                                 hipStream_t stream);
 
 // ---- FFN workspace plan
 struct FfnShape {

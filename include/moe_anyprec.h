@@ -156,6 +156,22 @@ moe_status moe_alloc_bits(const float* gate, int32_t P, int32_t b_lo, int32_t b_
                           float target_avg_bits, uint8_t* bits, float* tau_out,
                           int32_t* n_hi_out, void* stream);
 
+/*
+ * Calibration-threshold mode (MatMoE review, Core Contribution: the routing
+ * score threshold is set on a calibration distribution of scores to meet the
+ * target average, then applied to each pair as it is routed):
+ *   bits[i] = b_max if gate[i] > tau (fp32 comparison), else b_lo
+ * for i < P.  A threshold calibrated once (for instance the tau_out of
+ * moe_alloc_bits over a calibration set of gate scores) is reused across
+ * decode steps, so a step's average width varies around the target instead
+ * of meeting it exactly.
+ *   gate [P] fp32 device, bits [P] uint8 device (output), tau host scalar
+ *   (-inf: every pair high).
+ * Ranges: P >= 0, 1 <= b_lo <= b_max <= 4, tau not NaN; else MOE_ERR_RANGE.
+ */
+moe_status moe_bits_from_threshold(const float* gate, int32_t P, float tau, int32_t b_lo, int32_t b_max,
+                                   uint8_t* bits, void* stream);
+
 /* n* computed on the host exactly as moe_alloc_bits does (pure). */
 int32_t moe_budget_pairs(int32_t P, int32_t b_lo, int32_t b_max, float target_avg_bits);
 

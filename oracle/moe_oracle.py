@@ -223,6 +223,27 @@ def threshold_interval(gates: np.ndarray, n: int):
     return lo, hi
 
 
+def calibrate_threshold(calib_gates: np.ndarray, b_lo: int, b_max: int, target) -> float:
+    """Threshold set on a calibration set of routing scores ([MAT] Core
+    Contribution: the threshold is calibrated on a score distribution to hit
+    the target average bit-width; Methodological Rigor: the average is met in
+    expectation).  Plain definition: the allocation rule of allocate_bits on
+    the calibration scores gives n high pairs; the threshold is the lowest
+    value whose strict upper set is those n, i.e. s_(n+1) of the sorted
+    scores (-inf when n is every score)."""
+    g = np.asarray(calib_gates, dtype=np.float64).ravel()
+    _, n, _ = allocate_bits(g, b_lo, b_max, target)
+    s = np.sort(g)[::-1]
+    return float(s[n]) if n < g.size else -math.inf
+
+
+def bits_from_threshold(gates: np.ndarray, tau: float, b_lo: int, b_max: int) -> np.ndarray:
+    """Widths from a fixed threshold: B_max where the score exceeds tau
+    (strictly, R8), B_lo elsewhere ([MAT] Core Contribution)."""
+    g = np.asarray(gates, dtype=np.float64).ravel()
+    return np.where(g > tau, b_max, b_lo).astype(np.int64)
+
+
 # ---------------------------------------------------------------------------
 # expert FFN
 

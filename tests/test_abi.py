@@ -122,6 +122,13 @@ def test_other_entry_points_validate(L):
     assert L.moe_residual_to_bf16(None, None, 0, None) == OK
     assert L.moe_residual_to_bf16(None, fake, 4, None) == NULL
     assert L.moe_residual_to_bf16(fake, fake, -1, None) == RANGE
+    assert L.moe_bits_from_threshold(None, 0, 0.5, 2, 4, None, None) == OK
+    assert L.moe_bits_from_threshold(fake, 4, 0.5, 2, 4, None, None) == NULL
+    assert L.moe_bits_from_threshold(fake, -1, 0.5, 2, 4, fake, None) == RANGE
+    assert L.moe_bits_from_threshold(fake, 4, float("nan"), 2, 4, fake, None) == RANGE
+    assert L.moe_bits_from_threshold(fake, 4, 0.5, 3, 2, fake, None) == RANGE
+    assert L.moe_bits_from_threshold(fake, 4, 0.5, 2, 5, fake, None) == RANGE
+    assert L.moe_bits_from_threshold(fake, 4, 0.5, 0, 4, fake, None) == RANGE
     assert L.moe_rmsnorm_to_bf16(None, None, 0, 2048, 1e-6, None) == OK
     assert L.moe_rmsnorm_to_bf16(None, fake, 4, 2048, 1e-6, None) == NULL
     assert L.moe_rmsnorm_to_bf16(fake, fake, -1, 2048, 1e-6, None) == RANGE

@@ -228,6 +228,51 @@ def test_alloc_sizes_and_ties(P):
 
 
 # ---------------------------------------------------------------------------
+# calibration-threshold mode: tau from the bisection over a calibration set,
+# then fixed widths on later batches
+
+
+@pytest.mark.parametrize("kind", ["routed", "ties"])
+def test_calibrated_threshold_and_fixed_widths(kind):
+    if kind == "routed":
+        # calibration gates of 16 decode batches of the Qwen shape, widths of 4 more
+        w, dev, _, _ = workload(2)
+        cfg = w.cfg
+        wr = dev["w_router"]
+        gates = []
+        for s in range(20):
+            x = bd.bf16_tensor(wl.step_activations(cfg, 500 + s, 32))
+            gates.append(bd.route(x, wr, None, cfg.k)[1].reshape(-1))
+        cal, held = torch.cat(gates[:16]), torch.cat(gates[16:])
+    else:
+        rng = np.random.default_rng(31)
+        cal = torch.from_numpy((rng.integers(0, 9, 5000) / 16).astype(np.float32)).cuda()
+        held = torch.from_numpy((rng.integers(0, 9, 3000) / 16).astype(np.float32)).cuda()
+    cal_np = cal.cpu().numpy().astype(np.float64)
+    held_np = held.cpu().numpy().astype(np.float64)
+    for target in (2.0, 2.5, 3.0, 3.3, 4.0):
+        note(f"calibrated threshold {kind} target={target}")
+        tau = torch.empty(1, dtype=torch.float32, device="cuda")
+        bd.alloc_bits(cal, 2, 4, target, tau=tau)
+        torch.cuda.synchronize()
+        tau_ref = orc.calibrate_threshold(cal_np, 2, 4, target)
+        assert float(tau.item()) == tau_ref, (target, tau.item(), tau_ref)
+        bits = bd.bits_from_threshold(held, float(tau.item()), 2, 4)
+        torch.cuda.synchronize()
+        ref = orc.bits_from_threshold(held_np, tau_ref, 2, 4)
+        assert np.array_equal(bits.cpu().numpy().astype(np.int64), ref)
+
+
+def test_fixed_widths_at_the_threshold_value():
+    # scores equal to tau stay low; -inf makes every pair high; empty input
+    g = torch.tensor([0.25, 0.5, 0.5, 0.75, 0.0, 1.0], dtype=torch.float32, device="cuda")
+    note("fixed widths at tau")
+    assert bd.bits_from_threshold(g, 0.5, 1, 4).cpu().tolist() == [1, 1, 1, 4, 1, 4]
+    assert bd.bits_from_threshold(g, float("-inf"), 2, 3).cpu().tolist() == [3] * 6
+    assert bd.bits_from_threshold(g[:0], 0.5, 2, 4).numel() == 0
+
+
+# ---------------------------------------------------------------------------
 # permutation: stable order by (expert, bits desc, pair id)
 
 

@@ -300,6 +300,45 @@ def test_round_bf16_matches_torch():
 
 
 # ---------------------------------------------------------------------------
+# calibration-threshold mode
+
+
+def test_calibrated_threshold_worked_example():
+    # scores 0.9, 0.5, 0.5, 0.2 at target 3.0 of {2, 4}: n* = 2, but the
+    # second and third scores tie, so one pair is high and tau = 0.5; later
+    # scores equal to tau stay low (strict comparison)
+    tau = orc.calibrate_threshold(np.array([0.9, 0.5, 0.5, 0.2]), 2, 4, 3.0)
+    assert tau == 0.5
+    assert orc.bits_from_threshold(np.array([0.6, 0.5, 0.4, 0.95]), tau, 2, 4).tolist() == [4, 2, 2, 4]
+
+
+def test_calibrated_threshold_reproduces_the_batch_rule_on_its_own_set():
+    # applied to the calibration set itself, the calibrated threshold gives
+    # exactly the per-batch allocation (ties included)
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        P = int(rng.integers(1, 300))
+        g = np.round(rng.random(P), int(rng.integers(1, 4)))   # coarse values: many ties
+        b_lo = int(rng.integers(1, 4))
+        tgt = b_lo + (4 - b_lo) * float(rng.random()) if trial % 5 else float(b_lo + (trial // 5) % 2 * (4 - b_lo))
+        tau = orc.calibrate_threshold(g, b_lo, 4, tgt)
+        ref, _, _ = orc.allocate_bits(g, b_lo, 4, tgt)
+        assert np.array_equal(orc.bits_from_threshold(g, tau, b_lo, 4), ref), (trial, P, b_lo, tgt)
+
+
+def test_calibrated_threshold_ends_and_expectation():
+    g = np.random.default_rng(22).random(1000)
+    assert orc.calibrate_threshold(g, 2, 4, 4.0) == -math.inf
+    assert np.all(orc.bits_from_threshold(g, orc.calibrate_threshold(g, 2, 4, 2.0), 2, 4) == 2)
+    # held-out scores of the same distribution meet the target in expectation
+    rng = np.random.default_rng(23)
+    cal, held = rng.random(200_000), rng.random(200_000)
+    for tgt in (2.5, 3.0, 3.5):
+        b = orc.bits_from_threshold(held, orc.calibrate_threshold(cal, 2, 4, tgt), 2, 4)
+        assert abs(b.mean() - tgt) < 0.01, (tgt, b.mean())
+
+
+# ---------------------------------------------------------------------------
 # stack: RMS-normalised bf16 layer input (a reading, not from the pages)
 
 
