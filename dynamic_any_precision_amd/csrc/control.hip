@@ -8,14 +8,11 @@
 // ranks every (token, expert) candidate across the block instead of k
 // arg-max rounds per token.
 //
-// Allocation by ranks: with n* the budget, the threshold tau of the
-// bisection (the smallest key whose strict upper set holds at most n*
-// pairs; MatMoE abstract item (3) and review, Core Contribution: binary
-// search for the threshold that meets the target average) gives a pair of
-// key v the high width exactly when #{keys >= v} <= n*: if that count fits,
-// a value just below v is a candidate threshold, so tau < v; if v > tau, the
-// pairs at or above v are among those above tau.  Each thread counts its
-// pair's rank against the P keys in LDS.
+// Allocation: the threshold tau of the bisection (the smallest key whose
+// strict upper set holds at most n* pairs; MatMoE abstract item (3) and
+// review, Core Contribution: binary search for the threshold that meets the
+// target average), found here by a radix descent over the P keys in LDS,
+// four passes of 8-bit digits instead of 32 one-bit steps.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan_dev.hpp"
@@ -108,34 +105,94 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
   }
   __syncthreads();
 
-  // allocation: high width iff #{keys >= own key} <= n*; the keys past P
-  // (up to a multiple of 8) read as 0, below every gate key.  Up to 256
-  // (512) pairs, four (two) adjacent threads split a pair's count over the
-  // key blocks.
-  for (int j = s.P + tid; j < ((s.P + 7) & ~7); j += PM_NT) skey[j] = 0u;
-  __syncthreads();
-  {
-    const int tpp = s.P <= PM_NT / 4 ? 4 : s.P <= PM_NT / 2 ? 2 : 1;  // threads per pair
-    const int i = tid / tpp, part = tid % tpp;
-    const int nblk = (s.P + 7) / 8;
-    int ge = 0;
-    if (i < s.P) {
-      const uint32_t v = skey[i];
-      const uint4* k4 = reinterpret_cast<const uint4*>(skey);
-      for (int j = part * nblk / tpp; j < (part + 1) * nblk / tpp; ++j) {
-        const uint4 a = k4[2 * j], b = k4[2 * j + 1];
-        ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
+  // Allocation (a block-uniform choice between two exact methods).
+  if (s.P <= PM_NT / 4) {
+    // Up to 256 pairs: high width iff #{keys >= own key} <= n*, counted by
+    // four adjacent threads per pair over the key blocks; the keys past P (up
+    // to a multiple of 8) read as 0, below every gate key.
+    for (int j = s.P + tid; j < ((s.P + 7) & ~7); j += PM_NT) skey[j] = 0u;
+    __syncthreads();
+    {
+      constexpr int tpp = 4;  // threads per pair
+      const int i = tid / tpp, part = tid % tpp;
+      const int nblk = (s.P + 7) / 8;
+      int ge = 0;
+      if (i < s.P) {
+        const uint32_t v = skey[i];
+        const uint4* k4 = reinterpret_cast<const uint4*>(skey);
+        for (int j = part * nblk / tpp; j < (part + 1) * nblk / tpp; ++j) {
+          const uint4 a = k4[2 * j], b = k4[2 * j + 1];
+          ge += (a.x >= v) + (a.y >= v) + (a.z >= v) + (a.w >= v) + (b.x >= v) + (b.y >= v) + (b.z >= v) + (b.w >= v);
+        }
+      }
+      ge += __shfl_xor(ge, 1, WAVE);
+      ge += __shfl_xor(ge, 2, WAVE);
+      if (i < s.P && part == 0) {
+        const int b = ge <= n_star ? b_max : b_lo;
+        bits_out[i] = (uint8_t)b;
+        L.sbits[i] = (uint8_t)b;
       }
     }
-    if (tpp >= 2) ge += __shfl_xor(ge, 1, WAVE);  // tpp is uniform over the block
-    if (tpp == 4) ge += __shfl_xor(ge, 2, WAVE);
-    if (i < s.P && part == 0) {
-      const int b = ge <= n_star ? b_max : b_lo;
-      bits_out[i] = (uint8_t)b;
-      L.sbits[i] = (uint8_t)b;
+    __syncthreads();
+  } else {
+    // More pairs: tau = the smallest key whose strict upper set holds at most
+    // n* pairs (the allocation kernel's bisection), found by a radix descent
+    // over 8-bit digits from the most significant: in each pass the digit is
+    // the smallest d for which the keys above the prefix plus the keys of the
+    // prefix's block with a digit above d number at most n* (a histogram of
+    // the block's digits and its suffix sums).  A pair is high iff its key
+    // exceeds tau.
+    {
+      __shared__ int hist[256];
+      __shared__ uint32_t s_prefix;
+      __shared__ int s_above;
+      const uint32_t myk = tid < s.P ? skey[tid] : 0u;
+      uint32_t prefix = 0u;
+      int above = 0;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+        if (tid < s.P && (myk & hmask) == prefix) atomicAdd(&hist[(myk >> shift) & 255u], 1);
+        __syncthreads();
+        if (wave == 0) {
+          const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+          const int ls = h0 + h1 + h2 + h3;
+          int suf = ls;  // sum over lanes >= this one
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) {
+            const int o = __shfl_down(suf, m, WAVE);
+            if (lane + m < 64) suf += o;
+          }
+          // S(d): pairs of the block with a digit above d
+          int sd[4];
+          sd[3] = suf - ls;
+          sd[2] = sd[3] + h3;
+          sd[1] = sd[2] + h2;
+          sd[0] = sd[1] + h1;
+          int dmin = 256;
+#pragma unroll
+          for (int i = 3; i >= 0; --i)
+            if (above + sd[i] <= n_star) dmin = 4 * lane + i;
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) dmin = min(dmin, __shfl_xor(dmin, m, WAVE));
+          if (lane == (dmin >> 2)) {
+            s_prefix = prefix | ((uint32_t)dmin << shift);
+            s_above = above + sd[dmin & 3];
+          }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        above = s_above;
+      }
+      if (tid < s.P) {
+        const int b = myk > prefix ? b_max : b_lo;
+        bits_out[tid] = (uint8_t)b;
+        L.sbits[tid] = (uint8_t)b;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // top-k never repeats an expert and allocation widths lie in [b_lo, b_max]
   plan_small_core(s, pp, L, 0);
