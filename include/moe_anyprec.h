@@ -53,7 +53,7 @@ typedef enum {
   MOE_ERR_ALIGN = 3,        /* a buffer is not 16-byte aligned                      */
   MOE_ERR_RANGE = 4,        /* an argument is outside its documented range          */
   MOE_ERR_WORKSPACE = 5,    /* workspace too small                                  */
-  MOE_ERR_UNSUPPORTED = 6,  /* valid but not supported by this build                */
+  MOE_ERR_UNSUPPORTED = 6,  /* valid but not supported by this library              */
   MOE_ERR_HIP = 7           /* a HIP call failed; see moe_last_hip_error()          */
 } moe_status;
 
