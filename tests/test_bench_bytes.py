@@ -35,3 +35,23 @@ def test_shared_expert_reads_its_widest_pair_once():
     io = 2 * 256 * 2 + 2 * 256 * 4 * 2 + 4 * 128 * 2 * 2
     assert total == planes + 3 * per_sz + io
     assert nact == 3 and bread == 7 / 3 and balloc == 2.0
+
+
+def test_recorded_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    # the counter record is used only for its own workload and while the
+    # kernel sources hash to the recorded value
+    rec = tmp_path / "rec.md"
+    rec.write_text(f"# x\n\nsource_sha256: {bench.ffn_source_hash()}\ntraffic_bytes_per_launch: 12345\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    assert bench.recorded_traffic(32, 3.0) == 12345.0
+    assert bench.recorded_traffic(1, 3.0) is None
+    assert bench.recorded_traffic(32, 2.5) is None
+    rec.write_text("source_sha256: 0000000000000000\ntraffic_bytes_per_launch: 12345\n")
+    assert bench.recorded_traffic(32, 3.0) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr
