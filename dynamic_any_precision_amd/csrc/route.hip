@@ -2,11 +2,12 @@
 // top-k.  ("routing each token to a small set of experts", DPA-MoE abstract;
 // "routing scores", MatMoE abstract.)
 //
-// Logits: grid (E/4 expert tiles, T/8 token tiles), 512 threads.  The eight
-// waves of a block split the hidden dimension; each accumulates the 4 x 8
+// Logits: grid (E/2 expert tiles, T/2 token tiles), 512 threads.  The eight
+// waves of a block split the hidden dimension; each accumulates the 2 x 2
 // (expert, token) dot products of its slice in float64 from exact bf16 /
 // fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
-// pair l, and wave 0 adds the eight slices in a fixed order.
+// pair l mod 4, and wave 0 adds the eight slices in a fixed order.  Small
+// tiles give many blocks: the kernel is latency-bound at decode sizes.
 // Prefill-sized batches (T >= 256) take the logits on the fp64 matrix cores
 // instead: one wave per 16-token x 16-expert tile, v_mfma_f64_16x16x4f64 over
 // the hidden dimension (the same exact products, accumulated in fp64).
@@ -20,8 +21,14 @@ namespace moe {
 
 namespace {
 
-constexpr int RT_TT = 8;  // tokens per block
-constexpr int RT_ET = 4;  // experts per block
+#ifndef RT_TT_N
+#define RT_TT_N 2
+#endif
+#ifndef RT_ET_N
+#define RT_ET_N 2
+#endif
+constexpr int RT_TT = RT_TT_N;  // tokens per block
+constexpr int RT_ET = RT_ET_N;  // experts per block
 constexpr int RT_WAVES = 8;
 
 template <int M, int N>
@@ -36,13 +43,15 @@ __device__ __forceinline__ void butterfly_step(double (&v)[N], int lane) {
   if constexpr (M > 1) butterfly_step<M / 2, N>(v, lane);
 }
 
-// Reduce-scatter of N = 32 values per lane: after the step with mask M,
-// v[0 .. M-1] hold partial sums of the indices selected by the lane's bits
-// below 32; the xor-32 step then folds the wave halves, so v[0] is the wave
-// total of index lane % 32.
-__device__ __forceinline__ void butterfly32(double (&v)[32], int lane) {
-  butterfly_step<16, 32>(v, lane);
-  v[0] += __shfl_xor(v[0], 32, WAVE);
+// Reduce-scatter of N values per lane (N a power of two <= 32): after the
+// step with mask M, v[0 .. M-1] hold partial sums of the indices selected by
+// the lane's bits below N; the xor steps from N up then fold the wave's
+// groups of N lanes, so v[0] is the wave total of index lane % N.
+template <int N>
+__device__ __forceinline__ void butterfly(double (&v)[N], int lane) {
+  butterfly_step<N / 2, N>(v, lane);
+#pragma unroll
+  for (int m = N; m < WAVE; m <<= 1) v[0] += __shfl_xor(v[0], m, WAVE);
 }
 
 // One wave per token.
@@ -99,11 +108,11 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_route_logits(const uint16_t* 
       }
     }
   }
-  static_assert(RT_ET * RT_TT == 32, "reduce-scatter width");
-  butterfly32(acc, lane);
+  static_assert(RT_ET * RT_TT <= 32 && (RT_ET * RT_TT & (RT_ET * RT_TT - 1)) == 0, "reduce-scatter width");
+  butterfly<RT_ET * RT_TT>(acc, lane);
   part[wave][lane] = acc[0];
   __syncthreads();
-  if (wave == 0 && lane < 32) {
+  if (wave == 0 && lane < RT_ET * RT_TT) {
     const int ee = lane / RT_TT, tt = lane % RT_TT;
     const int e = e0 + ee, t = t0 + tt;
     if (e < E && tt < nt) {
