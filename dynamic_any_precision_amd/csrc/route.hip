@@ -30,6 +30,9 @@ namespace {
 constexpr int RT_TT = RT_TT_N;  // tokens per block
 constexpr int RT_ET = RT_ET_N;  // experts per block
 constexpr int RT_WAVES = 8;
+#ifndef RT_TOPK_WAVES
+#define RT_TOPK_WAVES 1  // waves (tokens) per top-k block: one, so the tokens spread over the CUs
+#endif
 
 template <int M, int N>
 __device__ __forceinline__ void butterfly_step(double (&v)[N], int lane) {
@@ -192,7 +195,8 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, 
 
 hipError_t launch_route_topk(const double* logits, int T, int E, int k, int renorm, int* idx, float* gate,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, renorm, idx, gate);
+  hipLaunchKernelGGL(k_route_topk, dim3((T + RT_TOPK_WAVES - 1) / RT_TOPK_WAVES), dim3(64 * RT_TOPK_WAVES), 0, stream,
+                     logits, T, E, k, renorm, idx, gate);
   return hipGetLastError();
 }
 
