@@ -2,11 +2,12 @@
 // top-k.  ("routing each token to a small set of experts", DPA-MoE abstract;
 // "routing scores", MatMoE abstract.)
 //
-// Logits: grid (E/2 expert tiles, T/2 token tiles), 512 threads.  The eight
-// waves of a block split the hidden dimension; each accumulates the 2 x 2
-// (expert, token) dot products of its slice in float64 from exact bf16 /
-// fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice sum of
-// pair l mod 4, and wave 0 adds the eight slices in a fixed order.  Small
+// Logits: grid (E/2 expert tiles, T/2 or T/4 token tiles), 512 threads.  The
+// eight waves of a block split the hidden dimension; each accumulates the
+// (expert, token) dot products of its tile and slice in float64 from exact
+// bf16 / fp32 inputs, a butterfly reduce-scatter leaves lane l with the slice
+// sum of pair l mod (tile size), and wave 0 adds the eight slices in a fixed
+// order.  Small
 // tiles give many blocks: the kernel is latency-bound at decode sizes.
 // Prefill-sized batches (T >= 256) take the logits on the fp64 matrix cores
 // instead: one wave per 16-token x 16-expert tile, v_mfma_f64_16x16x4f64 over
@@ -21,14 +22,9 @@ namespace moe {
 
 namespace {
 
-#ifndef RT_TT_N
-#define RT_TT_N 2
-#endif
-#ifndef RT_ET_N
-#define RT_ET_N 2
-#endif
-constexpr int RT_TT = RT_TT_N;  // tokens per block
-constexpr int RT_ET = RT_ET_N;  // experts per block
+// logits tiles (tokens x experts per block): about a thousand blocks at
+// decode sizes -- 2 x 2 up to 32 tokens, 4 x 2 above
+constexpr int RT_ET = 2;
 constexpr int RT_WAVES = 8;
 #ifndef RT_TOPK_WAVES
 #define RT_TOPK_WAVES 1  // waves (tokens) per top-k block: one, so the tokens spread over the CUs
@@ -68,6 +64,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
              threadIdx.x & 63);
 }
 
+template <int RT_TT>
 __global__ __launch_bounds__(RT_WAVES * 64) void k_route_logits(const uint16_t* __restrict__ x, int T, int d,
                                                       const float* __restrict__ W, int E,
                                                       const float* __restrict__ bias, double* __restrict__ logits) {
@@ -188,8 +185,13 @@ hipError_t launch_route_logits(const uint16_t* x, int T, int d, const float* W, 
     hipLaunchKernelGGL(k_route_logits_mfma, grid, dim3(256), 0, stream, x, T, d, W, E, bias, logits);
     return hipGetLastError();
   }
-  dim3 grid((E + RT_ET - 1) / RT_ET, (T + RT_TT - 1) / RT_TT);
-  hipLaunchKernelGGL(k_route_logits, grid, dim3(RT_WAVES * 64), 0, stream, x, T, d, W, E, bias, logits);
+  if (T <= 32) {
+    dim3 grid((E + RT_ET - 1) / RT_ET, (T + 1) / 2);
+    hipLaunchKernelGGL(k_route_logits<2>, grid, dim3(RT_WAVES * 64), 0, stream, x, T, d, W, E, bias, logits);
+  } else {
+    dim3 grid((E + RT_ET - 1) / RT_ET, (T + 3) / 4);
+    hipLaunchKernelGGL(k_route_logits<4>, grid, dim3(RT_WAVES * 64), 0, stream, x, T, d, W, E, bias, logits);
+  }
   return hipGetLastError();
 }
 
