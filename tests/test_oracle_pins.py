@@ -482,3 +482,147 @@ def test_fixture_determinism():
     assert np.array_equal(a.routed.w13_planes, b.routed.w13_planes)
     assert np.array_equal(a.routed.w2_sz, b.routed.w2_sz)
     assert np.array_equal(a.w_router, b.w_router)
+
+
+# ---------------------------------------------------------------------------
+# shared experts, renormalised gates, logit bias
+
+
+@pytest.fixture(scope="module")
+def tiny_shared():
+    # the tiny layer with two always-on shared experts of intermediate 128
+    return wl.make_workload(wl.config(1, n_shared=2, f_shared=128))
+
+
+def _shared_reference(w, tokens):
+    """Sum over the shared experts of a plain 4-bit group-quantised SwiGLU MLP
+    with weight 1 (DeepSeekMoE-16B-shaped config: two always-on shared experts
+    read at 4 bits), dense torch float64 from the encoder's codes; h rounded
+    to bfloat16 by torch."""
+    bank = w.shared
+    g, f = bank.g, bank.f
+    X = torch.from_numpy(wl.bf16_bits_to_f32(w.x_bf16).astype(np.float64))
+    out = torch.zeros(len(tokens), w.cfg.d, dtype=torch.float64)
+    for s in range(bank.n_experts):
+        W13 = torch.from_numpy((bank.q13[s].astype(np.float64) - np.repeat(bank.z13[s], g, -1))
+                               * np.repeat(bank.s13[s], g, -1).astype(np.float64))
+        W2 = torch.from_numpy((bank.q2[s].astype(np.float64) - np.repeat(bank.z2[s], g, -1))
+                              * np.repeat(bank.s2[s], g, -1).astype(np.float64))
+        for i, t in enumerate(tokens):
+            gu = W13 @ X[t]
+            h = torch.nn.functional.silu(gu[:f]) * gu[f:]
+            h = h.to(torch.bfloat16).to(torch.float64)   # bf16 RNE of the fp64 value
+            out[i] += W2 @ h
+    return out.numpy()
+
+
+def test_shared_experts_alone_equal_plain_4bit_swiglu(tiny_shared):
+    # With every routed gate zero only the shared term is left, and it is each
+    # shared expert's full-width SwiGLU with weight 1.  Reading the shared
+    # experts at B_lo, or weighting them by any gate, fails this.
+    w = tiny_shared
+    cfg = w.cfg
+    idx, gate, _, _ = orc.route(w.x_bf16, w.w_router, None, cfg.k)
+    bits, _, _ = orc.allocate_bits(gate, cfg.b_lo, cfg.b_max, cfg.target)
+    rc, sc = orc.bank_cache(w.routed), orc.bank_cache(w.shared)
+    tokens = [0, 5, 15]
+    y0 = orc.combine(w.x_bf16, idx, np.zeros_like(gate), bits, rc, sc, cfg.n_shared, tokens)
+    ref = _shared_reference(w, tokens)
+    # fp64 bf16 rounding of h may differ from torch's fp64->bf16 only on exact ties
+    assert np.allclose(y0[tokens], ref, rtol=1e-12, atol=1e-14)
+    # a shared expert read at B_lo (2 planes) instead is far from it
+    lo = sum(orc.expert_ffn(wl.bf16_bits_to_f32(w.x_bf16[0]).astype(np.float64), *sc.weights(s, 2))
+             for s in range(cfg.n_shared))
+    assert np.linalg.norm(lo - ref[0]) > 1e-2 * np.linalg.norm(ref[0])
+
+
+def test_shared_term_does_not_depend_on_the_gates(tiny_shared):
+    # y(a * gates) = y_shared + a * y_routed: the shared term is weight 1 and
+    # the routed term is linear in the gates, so y(2g) - y(g) = y(g) - y(0).
+    w = tiny_shared
+    cfg = w.cfg
+    idx, gate, _, _ = orc.route(w.x_bf16, w.w_router, None, cfg.k)
+    bits, _, _ = orc.allocate_bits(gate, cfg.b_lo, cfg.b_max, cfg.target)
+    rc, sc = orc.bank_cache(w.routed), orc.bank_cache(w.shared)
+    y = {a: orc.combine(w.x_bf16, idx, a * gate, bits, rc, sc, cfg.n_shared) for a in (0.0, 1.0, 2.0)}
+    assert np.allclose(y[2.0] - y[1.0], y[1.0] - y[0.0], rtol=1e-10, atol=1e-13)
+    routed_only = orc.combine(w.x_bf16, idx, gate, bits, rc)
+    assert np.allclose(y[1.0] - y[0.0], routed_only, rtol=1e-10, atol=1e-13)
+    assert np.linalg.norm(y[0.0]) > 0
+
+
+def _router_from_logits(logits_row):
+    """A one-token router whose logits are the given small integers exactly:
+    x = [1.0] (bf16), W_r = the logits as a column."""
+    x = wl.f32_to_bf16_bits(np.ones((1, 1), dtype=np.float32))
+    W = np.asarray(logits_row, dtype=np.float32)[:, None]
+    return x, W
+
+
+def test_renorm_hand_worked_three_experts():
+    # logits (0, 1, 2), top-2 = experts 2, 1.  Softmax over all three:
+    # e^2/(1+e+e^2) = 0.66524095577..., e/(1+e+e^2) = 0.24472847105...
+    # Renormalised over the chosen two: e^2/(e+e^2) = e/(1+e) = 0.73105857863...,
+    # 1/(1+e) = 0.26894142137...
+    x, W = _router_from_logits([0.0, 1.0, 2.0])
+    idx, gate, _, _ = orc.route(x, W, None, 2, renorm=False)
+    assert idx.tolist() == [[2, 1]]
+    assert np.allclose(gate[0], [0.6652409557748219, 0.24472847105479764], rtol=1e-15, atol=0)
+    idx, gate, _, _ = orc.route(x, W, None, 2, renorm=True)
+    assert idx.tolist() == [[2, 1]]
+    assert np.allclose(gate[0], [0.7310585786300049, 0.2689414213699951], rtol=1e-15, atol=0)
+
+
+def test_renorm_equals_softmax_over_chosen_logits(tiny):
+    # Closed form: renormalised gates are the softmax taken over the top-k
+    # logits alone (the common factor 1/sum over all experts cancels).
+    cfg = tiny.cfg
+    idx, gate, _, l = orc.route(tiny.x_bf16, tiny.w_router, None, cfg.k, renorm=True)
+    idx0, gate0, _, _ = orc.route(tiny.x_bf16, tiny.w_router, None, cfg.k, renorm=False)
+    assert np.array_equal(idx, idx0)
+    for t in range(cfg.T):
+        lk = np.array([l[t, e] for e in idx[t]])
+        ref = np.exp(lk - lk.max()) / np.exp(lk - lk.max()).sum()
+        assert np.allclose(gate[t], ref, rtol=1e-13, atol=0)
+        assert math.isclose(gate[t].sum(), 1.0, abs_tol=1e-15)
+        # ratios between chosen experts are unchanged by renormalisation
+        assert math.isclose(gate[t, 0] / gate[t, 1], gate0[t, 0] / gate0[t, 1], rel_tol=1e-13)
+
+
+def test_logit_bias_hand_worked():
+    # zero router weights and bias (0, 1, 2): the logits are the bias, so the
+    # gates are those of the hand-worked three-expert case above
+    x = wl.f32_to_bf16_bits(np.ones((1, 4), dtype=np.float32))
+    W = np.zeros((3, 4), dtype=np.float32)
+    bias = np.array([0.0, 1.0, 2.0], dtype=np.float32)
+    l = orc.router_logits(x, W, bias)
+    assert l.tolist() == [[0.0, 1.0, 2.0]]
+    idx, gate, _, _ = orc.route(x, W, bias, 2)
+    assert idx.tolist() == [[2, 1]]
+    assert np.allclose(gate[0], [0.6652409557748219, 0.24472847105479764], rtol=1e-15, atol=0)
+    # a bias large enough reorders the choice
+    idx, _, _, _ = orc.route(x, W, np.array([5.0, 1.0, 2.0], dtype=np.float32), 2)
+    assert idx.tolist() == [[0, 2]]
+
+
+def test_logit_bias_is_an_extra_input_column_of_ones():
+    # Identity: adding bias_e equals appending a constant-1 input column whose
+    # router weight for expert e is bias_e.  Checked on the prefill layer's
+    # Zipf-style bias (the device the prefill workload uses) on 8 experts.
+    rng = np.random.default_rng(3)
+    T, d = 8, 256
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    W8 = (rng.standard_normal((8, d)) * 0.02).astype(np.float32)
+    bias = wl.make_workload(wl.config(1, zipf_bias=True)).logit_bias
+    x1 = np.concatenate([x, wl.f32_to_bf16_bits(np.ones((T, 1), dtype=np.float32))], axis=1)
+    W1 = np.concatenate([W8, bias[:, None]], axis=1)
+    la = orc.router_logits(x, W8, bias)
+    lb = orc.router_logits(x1, W1, None)
+    assert np.allclose(la, lb, rtol=0, atol=1e-12)
+    ia, ga, _, _ = orc.route(x, W8, bias, 2)
+    ib, gb, _, _ = orc.route(x1, W1, None, 2)
+    assert np.array_equal(ia, ib)
+    assert np.allclose(ga, gb, rtol=1e-12, atol=0)
+    # and the bias does change the routing of this batch
+    ic, _, _, _ = orc.route(x, W8, None, 2)
+    assert not np.array_equal(ia, ic)
