@@ -168,9 +168,9 @@ def route_workspace_bytes(T: int, E: int) -> int:
 
 
 def route_workspace(T: int, E: int, device="cuda") -> torch.Tensor:
-    """Zero-filled router workspace (its counters must start at zero)."""
+    """Router workspace (any content: it receives the T x E float64 logits)."""
     n = route_workspace_bytes(T, E)
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def route(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torch.Tensor], top_k: int,

@@ -32,6 +32,14 @@
  *     token's top-k) never make a kernel read or write out of bounds: such
  *     pairs are dropped from the output (of duplicates, the first pair with a
  *     valid width is kept).
+ *   - Where this interface departs from the plainest layer signature:
+ *     the plane words are tiled (16-row tiles, 128-column blocks, see the
+ *     bank struct) instead of row-major [N][K/32], and (scale, zero) is
+ *     [N/16][K/group][2][16] instead of [N][K/group][2], so one 64-lane
+ *     load reads a whole matrix-core operand; moe_route takes a workspace
+ *     for its float64 logits; top_k is at most 8 (the combine keeps a
+ *     token's slots in registers); `stream` is a void* so that the header
+ *     needs no HIP include.
  *   - No C++ exception crosses the ABI.  The library keeps no state between
  *     calls except a cached device property, so calls are thread-safe; calls
  *     that share a workspace must be ordered on one stream.
@@ -119,8 +127,8 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E);
  *   topk_idx   [T][top_k] int32 (output)
  *   topk_gate  [T][top_k] fp32  (output)
  *   workspace  >= moe_route_workspace_bytes(T, E) bytes, 16-byte aligned,
- *              zero-filled before its first use; every completed call
- *              leaves its counters zero again, so it can be reused.
+ *              any content: it receives the T x E float64 logits and is
+ *              overwritten by every call (reusable without clearing).
  * Ranges: T >= 0 (T == 0 is a no-op), d multiple of 128, 1 <= E <= 256,
  * 1 <= top_k <= min(E, 8).
  */
