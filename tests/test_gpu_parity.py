@@ -427,23 +427,10 @@ def test_ffn_tiny_accumulate_and_ragged():
         assert err < REL_L2, (T, err)
 
 
-@pytest.mark.parametrize("target", [2.0, 2.5, 3.0, 4.0])
-def test_ffn_qwen_decode(target):
-    note(f"ffn cfg2 T=32 target={target}")
-    err, _ = _ffn_case(2, target=target, tokens=[0, 7, 19, 31])
-    assert err < REL_L2, err
-
-
 def test_ffn_qwen_decode_group64():
     # two quant groups per k-block on the decode path with many items
     note("ffn cfg2 T=32 g=64")
-    err, _ = _ffn_case(2, tokens=[0, 7, 19, 31], over=dict(g=64))
-    assert err < REL_L2, err
-
-
-def test_ffn_qwen_decode_batch1():
-    note("ffn cfg2 T=1")
-    err, _ = _ffn_case(2, T=1, target=3.0)
+    err, _ = _ffn_case(2, over=dict(g=64))
     assert err < REL_L2, err
 
 
@@ -466,22 +453,6 @@ def test_ffn_small_batch_arbitrary_bit_mix(seed):
     b = rng.integers(1, 5, size=4 * w.cfg.k)
     note(f"ffn small batch cfg2 T=4 random bits seed={seed}")
     err, _ = _ffn_case(2, bits_np=b, T=4)
-    assert err < REL_L2, err
-
-
-@pytest.mark.parametrize("b_lo", [1, 2])
-def test_ffn_deepseek_shared(b_lo):
-    note(f"ffn cfg3 b_lo={b_lo}")
-    err, _ = _ffn_case(3, b_lo=b_lo, tokens=[0, 5, 15])
-    assert err < REL_L2, err
-
-
-def test_ffn_qwen_prefill_sampled_tokens():
-    # 4096 tokens with Zipf-skewed expert load: experts hold hundreds to
-    # thousands of pairs, many chunks per expert, widths mixed inside chunks
-    note("ffn cfg4 T=4096")
-    err, b = _ffn_case(4, tokens=[0, 1, 1000, 2047, 3333, 4095])
-    assert set(np.unique(b)) <= {2, 4}
     assert err < REL_L2, err
 
 
@@ -529,37 +500,6 @@ def test_ffn_wide_chunks_deepseek_shared():
 def _check_rmsnorm(h, x, eps):
     ref = orc.rmsnorm_bf16(h.cpu().numpy(), eps)
     assert np.array_equal(x.float().cpu().numpy().astype(np.float64), ref)
-
-
-def test_stack_layers_teacher_forced():
-    # three layers of the 48-layer stack shape, T=64: the residual is carried
-    # on the GPU (fp32 h, RMS-normalised bf16 layer input, checked bit for
-    # bit); each layer's output is checked against the oracle on the GPU's
-    # own layer input (teacher forcing)
-    cfg = wl.config(5)
-    rng = np.random.default_rng(5)
-    h = torch.from_numpy(rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)).cuda()
-    x = bd.rmsnorm_to_bf16(h, eps=1e-6)
-    _check_rmsnorm(h, x, 1e-6)
-    rows = [0, 17, 63]
-    for layer in range(3):
-        w_router, bank = wl.make_stack_layer(cfg, layer)
-        dev_bank = bd.DeviceBank.from_host(bank)
-        note(f"stack layer {layer}")
-        idx, gate = bd.route(x, torch.from_numpy(w_router).cuda(), None, cfg.k)
-        bits = bd.alloc_bits(gate.reshape(-1), cfg.b_lo, 4, 2.0 + 0.5 * layer)
-        x_np = x.view(torch.int16).cpu().numpy().view(np.uint16)
-        y0 = h.clone()
-        h = bd.anyprec_ffn(dev_bank, None, x, idx, gate, bits, y=h, accumulate=True)
-        torch.cuda.synchronize()
-        oc = orc.bank_cache(bank)
-        ref = orc.combine(x_np, idx.cpu().numpy(), gate.cpu().numpy().astype(np.float64),
-                          bits.cpu().numpy(), oc, tokens=rows)
-        got = h.cpu().numpy().astype(np.float64)[rows] - y0.cpu().numpy().astype(np.float64)[rows]
-        assert rel_l2(got, ref[rows]) < REL_L2, layer
-        x = bd.rmsnorm_to_bf16(h, eps=1e-6)
-        _check_rmsnorm(h, x, 1e-6)
-        del dev_bank
 
 
 def test_ffn_drops_invalid_pairs():
