@@ -5,9 +5,17 @@ layer of the 48-layer stack (teacher-forced).
 
 Bars: routing indices and per-pair widths bit-exact (top-k ties flagged
 where the oracle's logit gap is below 1e-5; widths from the oracle's
-allocation on the GPU's own gates); every checked output row, and all of
-them together, within relative L2 1e-3.  Each case prints its largest row
-error."""
+allocation on the GPU's own gates); all checked output rows together within
+relative L2 1e-3, and every single row within 5e-3.  Each case prints its
+largest row error.
+
+The per-row bar follows from the arithmetic.  The SwiGLU output h is rounded
+to bf16 on both sides, from fp32 sums on the GPU and fp64 sums in the
+oracle; where the two land on different sides of a bf16 rounding boundary
+the element differs by one bf16 step (2^-8 relative), which moves its row
+by about 2^-8 |h_j| / ||h|| (1.4e-4 for a typical element of 768, near 1e-3
+for the largest of a row).  A handful of such steps in one row stays below
+5e-3, while a pair read at a wrong width moves its row by 1e-1 or more."""
 import multiprocessing as mp
 import sys
 
@@ -23,6 +31,7 @@ import oracle_pool
 pytestmark = pytest.mark.gpu
 
 REL_L2 = 1e-3
+ROW_REL_L2 = 5e-3
 TIE_GAP = 1e-5
 
 
@@ -44,7 +53,7 @@ def check_rows(name, got, ref):
     print(f"[parity] {name}: rows={per_row.size} overall_rel_l2={overall:.3e} "
           f"max_row_rel_l2={per_row.max():.3e} median_row_rel_l2={np.median(per_row):.3e}", flush=True)
     assert overall < REL_L2, (name, overall)
-    assert per_row.max() < REL_L2, (name, int(per_row.argmax()), float(per_row.max()))
+    assert per_row.max() < ROW_REL_L2, (name, int(per_row.argmax()), float(per_row.max()))
     return per_row
 
 
@@ -256,16 +265,20 @@ def test_stack48_every_layer_teacher_forced():
     torch.cuda.empty_cache()
     note(f"stack48: oracle on {N_LAYERS} layers in {oracle_pool.pool_size()} worker processes")
     ctx = mp.get_context("spawn")
+    refs = {}
     with ctx.Pool(oracle_pool.pool_size()) as pool:
-        refs = dict(pool.imap_unordered(oracle_pool.stack_layer, sorted(tasks.items())))
-    worst = {}
+        for l, out in pool.imap_unordered(oracle_pool.stack_layer, sorted(tasks.items())):
+            refs[l] = out
+            note(f"stack48: oracle layer {l} done ({len(refs)}/{N_LAYERS})")
     for target in targets:
         errs = []
         for l in range(N_LAYERS):
             per_row = row_rel_l2(got_of[(l, target)], refs[l][target])
             errs.append(per_row.max())
-            assert per_row.max() < REL_L2, (l, target, per_row)
-        worst[target] = max(errs)
+            assert per_row.max() < ROW_REL_L2, (l, target, per_row)
+        overall = np.concatenate([got_of[(l, target)] - refs[l][target] for l in range(N_LAYERS)])
+        norm = np.concatenate([refs[l][target] for l in range(N_LAYERS)])
+        assert np.linalg.norm(overall) / np.linalg.norm(norm) < REL_L2, target
         print(f"[parity] stack48 target={target}: max row rel-L2 over 48 layers {max(errs):.3e}, "
               f"final layer {errs[-1]:.3e}", flush=True)
     print(f"[parity] stack48 flagged router ties {flagged}", flush=True)
