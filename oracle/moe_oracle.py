@@ -349,3 +349,125 @@ def layer(x_bf16, w_router, logit_bias, k: int, b_lo: int, b_max: int, target,
     bits, n, ns = allocate_bits(gate, b_lo, b_max, target)
     y = combine(x_bf16, idx, gate, bits, routed, shared, n_shared, tokens)
     return dict(idx=idx, gate=gate, gap=gap, logits=logits, bits=bits, n_hi=n, n_star=ns, y=y)
+
+
+# ---------------------------------------------------------------------------
+# DuoRate: per-expert read widths from a baked distortion tensor, a
+# label-free prefill profile and a Lagrangian rate-distortion solve under the
+# decode rate ([DUO] abstract).
+
+
+def distortion_tensor(cache: DequantCache, experts=None) -> np.ndarray:
+    """The baked distortion tensor: Delta[e, b-1, c] = sum over the rows n of
+    the gate/up matrix W13 of (W_hat^(B)[n, c] - W_hat^(b)[n, c])^2, the
+    squared change of input column c's weights when expert e is read at b
+    planes instead of the stored uniform tier of B planes ([DUO] abstract:
+    one uniform stored tier of a prefix-readable stream, a baked distortion
+    tensor).  Reading: the stored tier is the reference (the checkpoint holds
+    no other weights), and the tensor covers the expert's input projection,
+    whose input is the layer input a prefill can profile.  float64
+    [E, B, d]; rows of width B are zero."""
+    E = cache.p13.shape[0]
+    experts = range(E) if experts is None else experts
+    B = cache.b_max
+    out = np.zeros((E, B, cache.d))
+    for e in experts:
+        full = cache.weights(e, B)[0]
+        for b in range(1, B + 1):
+            diff = full - cache.weights(e, b)[0]
+            out[e, b - 1] = np.sum(diff * diff, axis=0)
+    return out
+
+
+def prefill_profile(x_bf16: np.ndarray, idx: np.ndarray, E: int):
+    """Label-free workload profile of a prefill batch ([DUO] abstract: it
+    profiles the workload's own prefill without labels): per expert the
+    number of routed pairs n[e] and the summed input energy
+    a[e, c] = sum over pairs (t, j) with idx[t, j] = e of x[t, c]^2."""
+    x = bf16_to_f64(x_bf16)
+    idx = np.asarray(idx)
+    a = np.zeros((E, x.shape[1]))
+    n = np.zeros(E, dtype=np.int64)
+    for t in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            a[e] += x[t] * x[t]
+            n[e] += 1
+    return a, n
+
+
+def expert_distortion(delta: np.ndarray, a: np.ndarray, n: np.ndarray) -> np.ndarray:
+    """Per-token distortion of expert e read at b planes on this workload:
+    Dbar[e, b-1] = <Delta[e, b-1], a[e]> / n[e] (one dot product per expert
+    and width, [DUO] abstract), the expected squared error of the expert's
+    gate/up pre-activations per routed token (diagonal approximation: input
+    channels treated as uncorrelated).  0 for an expert the prefill never
+    routes to."""
+    E, B, _ = delta.shape
+    D = np.zeros((E, B))
+    for e in range(E):
+        if n[e] > 0:
+            for b in range(B):
+                D[e, b] = float(np.dot(delta[e, b], a[e])) / float(n[e])
+    return D
+
+
+def rate_budget(n: np.ndarray, target) -> int:
+    """Budget of the decode rate in summed bits: floor(b* x sum_e n_e), exact
+    on the float32 value of the target."""
+    N = int(np.sum(n))
+    return math.floor(Fraction(float(np.float32(target))) * N)
+
+
+def lagrangian_widths(D: np.ndarray, lam: float, b_lo: int, b_max: int) -> np.ndarray:
+    """Per-expert decision at multiplier lam: b_e = argmin over widths
+    b in [b_lo, b_max] of Dbar[e, b-1] + lam * b, evaluated as
+    fl(Dbar + fl(lam * b)) in float64, ties to the smaller width.  The
+    routing frequency does not appear: in the decode functional
+    sum_e p_e (Dbar_e(b_e) + lam b_e) it is a common factor of each
+    expert's own terms ([DUO] abstract: it cancels from every per-expert
+    decision)."""
+    E = D.shape[0]
+    out = np.empty(E, dtype=np.int64)
+    for e in range(E):
+        best, bw = None, b_lo
+        for b in range(b_lo, b_max + 1):
+            c = float(D[e, b - 1]) + float(lam) * float(b)
+            if best is None or c < best:
+                best, bw = c, b
+        out[e] = bw
+    return out
+
+
+def duorate_widths(D: np.ndarray, n: np.ndarray, b_lo: int, b_max: int, target):
+    """Lagrangian rate-distortion allocation under the decode functional
+    ([DUO] abstract: solved by a bisection).  The decode rate of widths b_e
+    is sum_e n_e b_e over sum_e n_e (bits read per routed pair, in
+    expectation over the profiled routing).  lam* is the smallest
+    non-negative float64 whose widths meet the budget, found by bisection
+    over the bit patterns of non-negative doubles (monotone in value), with
+    the upper end lam_hi = 2 max_e Dbar[e, b_lo - 1] + 1, where every expert
+    takes b_lo.  Returns (widths [E], lam*)."""
+    budget = rate_budget(n, target)
+    n = np.asarray(n, dtype=np.int64)
+
+    def rate_ok(lam):
+        return int(np.sum(n * lagrangian_widths(D, lam, b_lo, b_max))) <= budget
+
+    lam_hi = 2.0 * float(np.max(D[:, b_lo - 1])) + 1.0
+    lo = 0
+    hi = int(np.float64(lam_hi).view(np.uint64))
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if rate_ok(float(np.uint64(mid).view(np.float64))):
+            hi = mid
+        else:
+            lo = mid + 1
+    lam = float(np.uint64(lo).view(np.float64))
+    return lagrangian_widths(D, lam, b_lo, b_max), lam
+
+
+def pair_bits_from_expert_widths(idx: np.ndarray, widths: np.ndarray) -> np.ndarray:
+    """Per-pair read widths of a decode batch: each pair reads its expert's
+    DuoRate width, b[t, j] = widths[idx[t, j]]."""
+    return np.asarray(widths)[np.asarray(idx)].ravel()
