@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
             "moe_rmsnorm_to_bf16": (i32, [vp, vp, i32, i32, f32, vp]),
             "moe_bits_from_threshold": (i32, [vp, i32, f32, i32, i32, vp, vp]),
             "moe_stream_read": (i32, [vp, i64, vp, vp]),
+            "moe_duorate_bake": (i32, [bp, vp, vp]),
+            "moe_duorate_profile": (i32, [vp, i32, i32, vp, i32, i32, vp, vp, vp]),
+            "moe_duorate_solve": (i32, [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp]),
+            "moe_bits_from_expert_widths": (i32, [vp, i32, vp, i32, vp, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
         }
@@ -323,6 +327,56 @@ def rmsnorm_to_bf16(h: torch.Tensor, x: Optional[torch.Tensor] = None, eps: floa
                                    _stream(stream))
     _check(st, "moe_rmsnorm_to_bf16")
     return x
+
+
+# ---------------------------------------------------------------------------
+# DuoRate per-expert widths
+
+
+def duorate_bake(bank: DeviceBank, stream=None) -> torch.Tensor:
+    """Distortion tensor [E][b_max][d] float64 of a bank (offline bake)."""
+    out = torch.empty(bank.n_experts, bank.b_max, bank.d, dtype=torch.float64, device=bank.w13_planes.device)
+    st = lib().moe_duorate_bake(ctypes.byref(bank.struct()), out.data_ptr(), _stream(stream))
+    _check(st, "moe_duorate_bake")
+    return out
+
+
+def duorate_profile(x: torch.Tensor, idx: torch.Tensor, E: int, stream=None):
+    """Prefill profile: (act_energy [E][d] float64, pair_count [E] int32)."""
+    T, d = x.shape
+    k = idx.shape[1]
+    a = torch.empty(E, d, dtype=torch.float64, device=x.device)
+    n = torch.empty(E, dtype=torch.int32, device=x.device)
+    st = lib().moe_duorate_profile(_ptr(x, _BF16, "x"), T, d, _ptr(idx, torch.int32, "topk_idx"), k, E,
+                                   a.data_ptr(), n.data_ptr(), _stream(stream))
+    _check(st, "moe_duorate_profile")
+    return a, n
+
+
+def duorate_solve(delta: torch.Tensor, act_energy: torch.Tensor, pair_count: torch.Tensor, b_lo: int, b_max: int,
+                  target: float, stream=None):
+    """Per-expert widths: (expert_bits [E] uint8, distortion [E][b_max] float64, lambda [1] float64)."""
+    E, B, d = delta.shape
+    D = torch.empty(E, B, dtype=torch.float64, device=delta.device)
+    w = torch.empty(E, dtype=torch.uint8, device=delta.device)
+    lam = torch.empty(1, dtype=torch.float64, device=delta.device)
+    st = lib().moe_duorate_solve(_ptr(delta, torch.float64, "delta"), _ptr(act_energy, torch.float64, "act_energy"),
+                                 _ptr(pair_count, torch.int32, "pair_count"), E, d, b_lo, b_max, float(target),
+                                 D.data_ptr(), w.data_ptr(), lam.data_ptr(), _stream(stream))
+    _check(st, "moe_duorate_solve")
+    return w, D, lam
+
+
+def bits_from_expert_widths(idx: torch.Tensor, expert_bits: torch.Tensor, bits: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    P = idx.numel()
+    if bits is None:
+        bits = torch.empty(P, dtype=torch.uint8, device=idx.device)
+    st = lib().moe_bits_from_expert_widths(_ptr(idx, torch.int32, "topk_idx"), P,
+                                           _ptr(expert_bits, torch.uint8, "expert_bits"), expert_bits.numel(),
+                                           _ptr(bits, torch.uint8, "bits"), _stream(stream))
+    _check(st, "moe_bits_from_expert_widths")
+    return bits
 
 
 STREAM_SINK = 8192

@@ -305,6 +305,49 @@ moe_status moe_rmsnorm_to_bf16(const float* h, uint16_t* x, int32_t rows, int32_
   return hip_status(moe::launch_rmsnorm_to_bf16(h, x, rows, d, eps, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_duorate_bake(const moe_expert_bank* bank, double* delta, void* stream) {
+  moe_status st = check_bank(bank, true);
+  if (st != MOE_OK) return st;
+  if (!delta) return MOE_ERR_NULL;
+  if (!aligned(delta, 8)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_duo_bake(w13_of(bank), bank->b_max, bank->group, bank->n_experts, delta,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_duorate_profile(const uint16_t* x, int32_t T, int32_t d, const int32_t* topk_idx, int32_t top_k,
+                               int32_t E, double* act_energy, int32_t* pair_count, void* stream) {
+  if (T < 0 || d < 1 || top_k < 1 || E < 1 || E > 1024) return MOE_ERR_RANGE;
+  if ((int64_t)T * top_k >= (1 << 30)) return MOE_ERR_RANGE;
+  if (!act_energy || !pair_count || (T > 0 && (!x || !topk_idx))) return MOE_ERR_NULL;
+  if (!aligned(act_energy, 8)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_duo_profile(x, T, d, topk_idx, top_k, E, act_energy, pair_count,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_duorate_solve(const double* delta, const double* act_energy, const int32_t* pair_count, int32_t E,
+                             int32_t d, int32_t b_lo, int32_t b_max, float target_rate, double* distortion,
+                             uint8_t* expert_bits, double* lambda_out, void* stream) {
+  if (E < 1 || E > 1024 || d < 1 || b_lo < 1 || b_max > 4 || b_lo > b_max) return MOE_ERR_RANGE;
+  if (!(target_rate >= (float)b_lo && target_rate <= (float)b_max)) return MOE_ERR_RANGE;
+  if (!delta || !act_energy || !pair_count || !distortion || !expert_bits) return MOE_ERR_NULL;
+  if (!aligned(delta, 8) || !aligned(act_energy, 8) || !aligned(distortion, 8)) return MOE_ERR_ALIGN;
+  // target = m * 2^-shift exactly (m a 24-bit integer)
+  int ex = 0;
+  const double fr = std::frexp((double)target_rate, &ex);
+  const long long m = (long long)std::ldexp(fr, 24);
+  const int shift = 24 - ex;
+  return hip_status(moe::launch_duo_solve(delta, act_energy, pair_count, E, d, b_max, b_lo, b_max, m, shift,
+                                          distortion, expert_bits, lambda_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_bits_from_expert_widths(const int32_t* topk_idx, int32_t P, const uint8_t* expert_bits, int32_t E,
+                                       uint8_t* bits, void* stream) {
+  if (P < 0 || E < 1) return MOE_ERR_RANGE;
+  if (P == 0) return MOE_OK;
+  if (!topk_idx || !expert_bits || !bits) return MOE_ERR_NULL;
+  return hip_status(moe::launch_bits_from_expert(topk_idx, P, expert_bits, E, bits, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (bytes < 0 || bytes % 16) return MOE_ERR_RANGE;
   if (bytes == 0) return MOE_OK;

@@ -72,6 +72,15 @@ hipError_t launch_ffn_w2(const FfnShape& s, const FfnLayout& L, char* ws, Matrix
 hipError_t launch_combine(const FfnShape& s, const FfnLayout& L, char* ws, const float* gate, float* y,
                           int accumulate, hipStream_t stream);
 
+// ---- DuoRate per-expert widths
+hipError_t launch_duo_bake(MatrixDev m, int B, int g, int E, double* delta, hipStream_t stream);
+hipError_t launch_duo_profile(const uint16_t* x, int T, int d, const int* idx, int k, int E, double* a, int* n,
+                              hipStream_t stream);
+hipError_t launch_duo_solve(const double* delta, const double* a, const int* n, int E, int d, int B, int b_lo,
+                            int b_max, long long tmant, int tshift, double* D, uint8_t* widths, double* lam_out,
+                            hipStream_t stream);
+hipError_t launch_bits_from_expert(const int* idx, int P, const uint8_t* w, int E, uint8_t* bits, hipStream_t stream);
+
 // ---- helpers
 hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream);
 hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream);

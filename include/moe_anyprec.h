@@ -261,6 +261,78 @@ moe_status moe_permute(const int32_t* topk_idx, const uint8_t* bits, int32_t T, 
                        int32_t* expert_maxbits, void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* DuoRate: per-expert read widths for a workload                            */
+/*
+ * "DuoRate: Two-Rate Per-Expert Precision Allocation for Mixture-of-Experts
+ * Serving" (abstract): the bank is stored once (one uniform tier of b_max
+ * prefix-readable planes); offline a distortion tensor is baked from it;
+ * online a prefill of the workload is profiled without labels, and each
+ * expert's decode read width is chosen by a Lagrangian rate-distortion
+ * solve under the decode rate (bits read per routed pair), in which routing
+ * frequency cancels from every per-expert decision, at the cost of one dot
+ * product per expert and width plus a bisection.  Decode steps then read
+ * every pair of expert e at width b_e (moe_bits_from_expert_widths feeds
+ * moe_anyprec_ffn unchanged).
+ */
+
+/*
+ * Bake the distortion tensor of a bank (offline):
+ *   delta[e][b-1][c] = sum over the 2*d_ff rows n of W13 of
+ *                      (s(n, c) * (q(n, c) - qhat_b(n, c)))^2,
+ * the squared change of input column c's gate/up weights when expert e is
+ * read at b planes instead of all b_max (qhat_b: the floor-and-compensation
+ * code of the first b planes; the zero-point terms of both reads cancel).
+ *   delta  [n_experts][b_max][d_model] float64, device, 8-byte aligned (output)
+ * Errors: those of the bank (see moe_expert_bank), MOE_ERR_NULL.
+ */
+moe_status moe_duorate_bake(const moe_expert_bank* bank, double* delta, void* stream);
+
+/*
+ * Profile a prefill batch (label-free): for every expert e,
+ *   pair_count[e]    = number of routed pairs (t, j) with topk_idx[t][j] == e,
+ *   act_energy[e][c] = sum over those pairs, in pair order, of x[t][c]^2 (float64).
+ *   x [T][d] bf16, topk_idx [T][top_k] int32 (entries outside [0, E) are
+ *   skipped), act_energy [E][d] float64 (output, 8-byte aligned),
+ *   pair_count [E] int32 (output).  All device.
+ * Ranges: T >= 0 (T == 0 writes zeros), d >= 1, top_k >= 1, 1 <= E <= 1024.
+ */
+moe_status moe_duorate_profile(const uint16_t* x, int32_t T, int32_t d, const int32_t* topk_idx, int32_t top_k,
+                               int32_t E, double* act_energy, int32_t* pair_count, void* stream);
+
+/*
+ * Solve for per-expert widths:
+ *   distortion[e][b-1] = <delta[e][b-1], act_energy[e]> / pair_count[e]
+ *                        (0 when pair_count[e] == 0), the expected squared
+ *                        error of the expert's gate/up pre-activations per
+ *                        routed token, for b = 1..b_max;
+ *   b_e(lam) = argmin over b in [b_lo, b_max] of distortion[e][b-1] + lam*b
+ *              (float64, no fused multiply-add, ties to the smaller b);
+ *   lam* = the smallest non-negative double with
+ *          sum_e pair_count[e] * b_e(lam) <= floor(target_rate * sum_e pair_count[e]),
+ *          found by bisection over the bit patterns of doubles in
+ *          [0, 2 * max_e distortion[e][b_lo-1] + 1];
+ *   expert_bits[e] = b_e(lam*); *lambda_out = lam* (if not NULL).
+ *   delta       [E][b_max][d] float64 as baked from a bank with this b_max
+ *   act_energy  [E][d] float64, pair_count [E] int32   (moe_duorate_profile)
+ *   distortion  [E][b_max] float64 (output), expert_bits [E] uint8 (output),
+ *   lambda_out  float64 scalar or NULL (output).  All device.
+ * Ranges: 1 <= E <= 1024, d >= 1, 1 <= b_lo <= b_max <= 4,
+ * b_lo <= target_rate <= b_max.
+ */
+moe_status moe_duorate_solve(const double* delta, const double* act_energy, const int32_t* pair_count, int32_t E,
+                             int32_t d, int32_t b_lo, int32_t b_max, float target_rate, double* distortion,
+                             uint8_t* expert_bits, double* lambda_out, void* stream);
+
+/*
+ * Per-pair widths of a batch from per-expert widths:
+ *   bits[i] = expert_bits[topk_idx[i]] for i < P (topk_idx viewed as [P]),
+ *   0 where the index is outside [0, E) (such pairs are dropped by the FFN).
+ * Ranges: P >= 0, E >= 1.
+ */
+moe_status moe_bits_from_expert_widths(const int32_t* topk_idx, int32_t P, const uint8_t* expert_bits, int32_t E,
+                                       uint8_t* bits, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Helpers                                                                   */
 
 /*
