@@ -471,3 +471,77 @@ def pair_bits_from_expert_widths(idx: np.ndarray, widths: np.ndarray) -> np.ndar
     """Per-pair read widths of a decode batch: each pair reads its expert's
     DuoRate width, b[t, j] = widths[idx[t, j]]."""
     return np.asarray(widths)[np.asarray(idx)].ravel()
+
+
+# ---------------------------------------------------------------------------
+# DPA-MoE: residual-aware chunk allocation over more than two widths
+# ([DPA] abstract: per-expert reconstruction residuals profiled offline;
+# chunks allocated at inference time from live router gate scores).  The
+# abstract gives no rule; the reading taken here is a proposal, stated in
+# each function.
+
+
+def expert_residuals(cache: DequantCache, experts=None) -> np.ndarray:
+    """Offline per-expert reconstruction residual at every width:
+    r[e, b-1] = ||W_hat^(B) - W_hat^(b)||_F^2 summed over both matrices of
+    expert e (gate/up and down), the stored uniform tier being the reference
+    (the checkpoint holds no other weights).  float64 [E, B]; r[:, B-1] = 0."""
+    E = cache.p13.shape[0]
+    experts = range(E) if experts is None else experts
+    B = cache.b_max
+    out = np.zeros((E, B))
+    for e in experts:
+        f13, f2 = cache.weights(e, B)
+        for b in range(1, B + 1):
+            w13, w2 = cache.weights(e, b)
+            out[e, b - 1] = float(np.sum((f13 - w13) ** 2)) + float(np.sum((f2 - w2) ** 2))
+    return out
+
+
+def chunk_scores(gates: np.ndarray, idx: np.ndarray, resid: np.ndarray, b_lo: int, b_max: int) -> np.ndarray:
+    """Score of reading chunk (plane) k of pair p, k = b_lo+1 .. b_max:
+    float32(g_p^2 * (r[e, k-2] - r[e, k-1])), the gate-weighted residual
+    the k-th plane removes (reading: a pair's output enters the layer output
+    scaled by its gate, so its squared error is scaled by g^2).  The product
+    is formed in float64 (g^2 of a float32 gate is exact there) and rounded
+    once to float32.  Returns [P, b_max - b_lo]."""
+    g = np.asarray(gates, dtype=np.float32).ravel().astype(np.float64)
+    e = np.asarray(idx).ravel()
+    P = g.size
+    out = np.empty((P, b_max - b_lo), dtype=np.float32)
+    for p in range(P):
+        for k in range(b_lo + 1, b_max + 1):
+            gain = float(resid[e[p], k - 2]) - float(resid[e[p], k - 1])
+            out[p, k - b_lo - 1] = np.float32((g[p] * g[p]) * gain)
+    return out
+
+
+def chunk_budget(P: int, b_lo: int, target) -> int:
+    """Extra planes beyond b_lo for P pairs: floor(P (b* - b_lo)), exact on
+    the float32 value of the target, clamped at 0."""
+    return max(0, math.floor(Fraction(P) * (Fraction(float(np.float32(target))) - b_lo)))
+
+
+def dpa_allocate(gates: np.ndarray, idx: np.ndarray, resid: np.ndarray, b_lo: int, b_max: int, target):
+    """Residual-aware allocation: every pair reads b_lo planes; the extra
+    planes go to the candidate chunks of highest score, as many as the budget
+    allows, never splitting equal scores (the rule of allocate_bits, applied
+    to the P (b_max - b_lo) candidate chunks).  A pair's width is b_lo plus
+    the number of its chunks chosen.  Plain definition by sorting.  Returns
+    (bits [P], chunks chosen, budget)."""
+    s = chunk_scores(gates, idx, resid, b_lo, b_max)
+    P = s.shape[0]
+    flat = s.astype(np.float64).ravel()
+    budget = min(chunk_budget(P, b_lo, target), flat.size)
+    srt = np.sort(flat)[::-1]
+    n = budget
+    while 0 < n < flat.size and srt[n - 1] == srt[n]:
+        n -= 1
+    if n == flat.size:
+        chosen = np.ones_like(flat, dtype=bool)
+    elif n == 0:
+        chosen = np.zeros_like(flat, dtype=bool)
+    else:
+        chosen = flat > srt[n]
+    bits = b_lo + chosen.reshape(s.shape).sum(axis=1)
+    return bits.astype(np.int64), int(chosen.sum()), budget
