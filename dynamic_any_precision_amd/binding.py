@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
             "moe_duorate_profile": (i32, [vp, i32, i32, vp, i32, i32, vp, vp, vp]),
             "moe_duorate_solve": (i32, [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp]),
             "moe_bits_from_expert_widths": (i32, [vp, i32, vp, i32, vp, vp]),
+            "moe_dpa_residuals_workspace_bytes": (sz, [bp]),
+            "moe_dpa_residuals": (i32, [bp, vp, vp, sz, vp]),
+            "moe_dpa_alloc_workspace_bytes": (sz, [i32, i32, i32]),
+            "moe_dpa_alloc": (i32, [vp, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
         }
@@ -376,6 +380,42 @@ def bits_from_expert_widths(idx: torch.Tensor, expert_bits: torch.Tensor, bits: 
                                            _ptr(expert_bits, torch.uint8, "expert_bits"), expert_bits.numel(),
                                            _ptr(bits, torch.uint8, "bits"), _stream(stream))
     _check(st, "moe_bits_from_expert_widths")
+    return bits
+
+
+# ---------------------------------------------------------------------------
+# DPA-MoE residual-aware chunk allocation
+
+
+def dpa_residuals(bank: DeviceBank, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-expert residuals [E][b_max] float64 of a bank (offline profile)."""
+    dev = bank.w13_planes.device
+    if workspace is None:
+        n = int(lib().moe_dpa_residuals_workspace_bytes(ctypes.byref(bank.struct())))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(bank.n_experts, bank.b_max, dtype=torch.float64, device=dev)
+    st = lib().moe_dpa_residuals(ctypes.byref(bank.struct()), out.data_ptr(), _ptr(workspace, name="workspace"),
+                                 workspace.numel(), _stream(stream))
+    _check(st, "moe_dpa_residuals")
+    return out
+
+
+def dpa_alloc(gate: torch.Tensor, idx: torch.Tensor, resid: torch.Tensor, b_lo: int, b_max: int, target: float,
+              bits: Optional[torch.Tensor] = None, n_chunks: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Residual-aware per-pair widths in [b_lo, b_max]."""
+    P = gate.numel()
+    E = resid.shape[0]
+    if workspace is None:
+        n = int(lib().moe_dpa_alloc_workspace_bytes(P, b_lo, b_max))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=gate.device)
+    if bits is None:
+        bits = torch.empty(P, dtype=torch.uint8, device=gate.device)
+    st = lib().moe_dpa_alloc(_ptr(gate, torch.float32, "gate"), _ptr(idx, torch.int32, "topk_idx"), P,
+                             _ptr(resid, torch.float64, "resid"), E, b_lo, b_max, float(target),
+                             _ptr(bits, torch.uint8, "bits"), _ptr(n_chunks, torch.int32, "n_chunks"),
+                             _ptr(workspace, name="workspace"), workspace.numel(), _stream(stream))
+    _check(st, "moe_dpa_alloc")
     return bits
 
 

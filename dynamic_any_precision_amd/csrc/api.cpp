@@ -348,6 +348,67 @@ moe_status moe_bits_from_expert_widths(const int32_t* topk_idx, int32_t P, const
   return hip_status(moe::launch_bits_from_expert(topk_idx, P, expert_bits, E, bits, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_dpa_residuals_workspace_bytes(const moe_expert_bank* bank) {
+  if (check_bank(bank, false) != MOE_OK) return 0;
+  return al256((size_t)bank->n_experts * bank->b_max * bank->d_model * 8) +
+         al256((size_t)bank->n_experts * bank->b_max * bank->d_ff * 8);
+}
+
+moe_status moe_dpa_residuals(const moe_expert_bank* bank, double* resid, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_bank(bank, true);
+  if (st != MOE_OK) return st;
+  if (!resid || !workspace) return MOE_ERR_NULL;
+  if (!aligned(resid, 8) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_dpa_residuals_workspace_bytes(bank)) return MOE_ERR_WORKSPACE;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  const int E = bank->n_experts, B = bank->b_max;
+  double* d13 = static_cast<double*>(workspace);
+  double* d2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + al256((size_t)E * B * bank->d_model * 8));
+  hipError_t e = moe::launch_duo_bake(w13_of(bank), B, bank->group, E, d13, strm);
+  if (e == hipSuccess) e = moe::launch_duo_bake(w2_of(bank), B, bank->group, E, d2, strm);
+  if (e == hipSuccess) e = moe::launch_resid_sum(d13, d2, E, B, bank->d_model, bank->d_ff, resid, strm);
+  return hip_status(e);
+}
+
+// floor(P * (target - b_lo)) exactly on the float value of target, clamped to [0, P * (b_max - b_lo)]
+static int64_t exact_chunk_budget(int32_t P, int32_t b_lo, int32_t b_max, float target) {
+  int ex = 0;
+  const double fr = std::frexp((double)target, &ex);
+  const __int128 m = (__int128)std::ldexp(fr, 24);
+  const int sh = 24 - ex;  // target = m / 2^sh, sh > 0 for targets below 2^24
+  __int128 num = (__int128)P * (m - ((__int128)b_lo << sh));
+  __int128 q = num >= 0 ? (num >> sh) : -((-num + ((__int128)1 << sh) - 1) >> sh);
+  if (q < 0) q = 0;
+  const __int128 cap = (__int128)P * (b_max - b_lo);
+  if (q > cap) q = cap;
+  return (int64_t)q;
+}
+
+size_t moe_dpa_alloc_workspace_bytes(int32_t P, int32_t b_lo, int32_t b_max) {
+  if (P < 0 || b_lo < 1 || b_max > 4 || b_lo > b_max) return 0;
+  const size_t n = (size_t)P * (b_max - b_lo);
+  return al256(n * 4) + al256(n) + 256;
+}
+
+moe_status moe_dpa_alloc(const float* gate, const int32_t* topk_idx, int32_t P, const double* resid, int32_t E,
+                         int32_t b_lo, int32_t b_max, float target_avg_bits, uint8_t* bits, int32_t* n_chunks_out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (P < 0 || E < 1 || b_lo < 1 || b_max > 4 || b_lo > b_max) return MOE_ERR_RANGE;
+  if (!(target_avg_bits >= (float)b_lo && target_avg_bits <= (float)b_max)) return MOE_ERR_RANGE;
+  if ((int64_t)P * (b_max - b_lo) >= (1 << 30)) return MOE_ERR_RANGE;
+  if (P == 0) return MOE_OK;
+  if (!gate || !topk_idx || !resid || !bits || !workspace) return MOE_ERR_NULL;
+  if (!aligned(resid, 8) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_dpa_alloc_workspace_bytes(P, b_lo, b_max)) return MOE_ERR_WORKSPACE;
+  const size_t n = (size_t)P * (b_max - b_lo);
+  float* scores = static_cast<float*>(workspace);
+  uint8_t* chosen = static_cast<uint8_t*>(workspace) + al256(n * 4);
+  const int64_t nc = exact_chunk_budget(P, b_lo, b_max, target_avg_bits);
+  return hip_status(moe::launch_dpa_alloc(gate, topk_idx, P, resid, E, b_max, b_lo, (int)nc, scores, chosen, bits,
+                                          n_chunks_out, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (bytes < 0 || bytes % 16) return MOE_ERR_RANGE;
   if (bytes == 0) return MOE_OK;

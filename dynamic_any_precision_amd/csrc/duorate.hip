@@ -20,6 +20,11 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Every floating-point operation of this file is rounded on its own: no
+// multiply-add contraction, so decisions taken on these values are the ones
+// any IEEE double (or float) evaluation of the same expressions takes.
+#pragma clang fp contract(off)
+
 namespace moe {
 namespace {
 
@@ -132,11 +137,12 @@ __global__ __launch_bounds__(256) void k_duo_distortion(const double* __restrict
 // ---------------------------------------------------------------------------
 // solve: one block, one thread per expert (E <= 1024).
 
+// The cost fl(D + fl(lam b)): a rounded product and a rounded sum.
 __device__ __forceinline__ int lag_width(const double* De, double lam, int b_lo, int b_max) {
   double best = 0.0;
   int bw = b_lo;
   for (int b = b_lo; b <= b_max; ++b) {
-    const double c = __dadd_rn(De[b - 1], __dmul_rn(lam, (double)b));
+    const double c = De[b - 1] + lam * (double)b;
     if (b == b_lo || c < best) {
       best = c;
       bw = b;
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(1024) void k_duo_solve(const double* __restrict__ D
   const long long N = block_sum_ll(ne, red_ll);
   const long long budget = (tmant * N) >> tshift;
   const double dmax = block_max_d(live ? De[b_lo - 1] : 0.0, red_d);
-  const double lam_hi = __dadd_rn(__dmul_rn(2.0, dmax), 1.0);
+  const double lam_hi = 2.0 * dmax + 1.0;
   unsigned long long lo = 0, hi = (unsigned long long)__double_as_longlong(lam_hi);
   while (lo < hi) {
     const unsigned long long mid = lo + (hi - lo) / 2;

@@ -81,6 +81,13 @@ hipError_t launch_duo_solve(const double* delta, const double* a, const int* n, 
                             hipStream_t stream);
 hipError_t launch_bits_from_expert(const int* idx, int P, const uint8_t* w, int E, uint8_t* bits, hipStream_t stream);
 
+// ---- DPA-MoE residual-aware chunk allocation
+hipError_t launch_resid_sum(const double* d13, const double* d2, int E, int B, int d, int f, double* resid,
+                            hipStream_t stream);
+hipError_t launch_dpa_alloc(const float* gate, const int* idx, int P, const double* resid, int E, int B, int b_lo,
+                            int n_chunks, float* scores, uint8_t* chosen, uint8_t* bits, int* n_chosen_out,
+                            hipStream_t stream);
+
 // ---- helpers
 hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream);
 hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream);

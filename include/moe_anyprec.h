@@ -333,6 +333,60 @@ moe_status moe_bits_from_expert_widths(const int32_t* topk_idx, int32_t P, const
                                        uint8_t* bits, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* DPA-MoE: residual-aware chunk allocation over widths b_lo..b_max          */
+/*
+ * "DPA-MoE: A Runtime Precision Control Framework for MoE Inference"
+ * (abstract): per-expert reconstruction residuals are profiled offline and
+ * chunks (planes) are allocated at inference time from live router gate
+ * scores, so one encoded checkpoint runs at many budgets.  The abstract
+ * states no rule; the one built here: every pair reads b_lo planes, and the
+ * extra planes go to the candidate (pair, plane) chunks that remove the most
+ * gate-weighted residual.
+ */
+
+/* Workspace bytes of moe_dpa_residuals (host, pure; 0 for an invalid bank). */
+size_t moe_dpa_residuals_workspace_bytes(const moe_expert_bank* bank);
+
+/*
+ * Offline residual profile of a bank:
+ *   resid[e][b-1] = ||W_hat^(b_max) - W_hat^(b)||_F^2 over both matrices of
+ *                   expert e (W13 and W2), float64, for b = 1..b_max
+ *                   (resid[e][b_max-1] = 0); the stored uniform tier is the
+ *                   reference.
+ *   resid  [n_experts][b_max] float64, device, 8-byte aligned (output)
+ *   workspace >= moe_dpa_residuals_workspace_bytes(bank), 256-byte aligned,
+ *   any content (per-column sums of both matrices).
+ */
+moe_status moe_dpa_residuals(const moe_expert_bank* bank, double* resid, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Workspace bytes of moe_dpa_alloc for P pairs (host, pure). */
+size_t moe_dpa_alloc_workspace_bytes(int32_t P, int32_t b_lo, int32_t b_max);
+
+/*
+ * Residual-aware widths of the P live routed pairs:
+ *   score(p, k) = fp32(fp64(gate[p])^2 * (resid[e][k-2] - resid[e][k-1])),
+ *                 e = topk_idx[p], for the extra planes k = b_lo+1..b_max
+ *                 (0 for an index outside [0, E));
+ *   budget      = floor(P * (target - b_lo)) extra planes, exact on the float
+ *                 target, at most P * (b_max - b_lo);
+ *   the candidates of highest score are chosen, as many as the budget allows
+ *   without splitting equal scores (the threshold bisection of
+ *   moe_alloc_bits, run over the candidates);
+ *   bits[p] = b_lo + number of chosen candidates of pair p;
+ *   *n_chunks_out = chosen candidates (device int32, or NULL).
+ *   gate [P] fp32, topk_idx [P] int32, resid [E][b_max] float64
+ *   (moe_dpa_residuals), bits [P] uint8 (output).  All device.
+ *   workspace >= moe_dpa_alloc_workspace_bytes(P, b_lo, b_max), 256-byte
+ *   aligned, any content.
+ * Ranges: P >= 0, E >= 1, 1 <= b_lo <= b_max <= 4, b_lo <= target <= b_max,
+ * P * (b_max - b_lo) < 2^30.
+ */
+moe_status moe_dpa_alloc(const float* gate, const int32_t* topk_idx, int32_t P, const double* resid, int32_t E,
+                         int32_t b_lo, int32_t b_max, float target_avg_bits, uint8_t* bits, int32_t* n_chunks_out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Helpers                                                                   */
 
 /*
