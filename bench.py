@@ -68,18 +68,36 @@ def log(msg):
 def algorithmic_ffn_bytes(idx, bits, cfg, accumulate=False):
     """Bytes the FFN stage must move: the first b_e planes and the (scale,
     zero) of every active expert (b_e = widest pair of the expert), the
-    activations in, the output, and the bf16 intermediate round trip."""
+    shared experts at full width, the activations in, the output, and the
+    bf16 intermediate round trip."""
+    k = kernel_bytes(idx, bits, cfg, accumulate)
+    return k["total"], k["bits_read"], k["bits_alloc"], k["n_active"]
+
+
+def kernel_bytes(idx, bits, cfg, accumulate=False):
+    """Algorithmic bytes of the FFN stage and of its two streaming kernels:
+    gate/up (W13 planes and (scale, zero) of the active experts, the shared
+    experts' W13, the activations in, the SwiGLU output written) and down
+    (W2 likewise, the SwiGLU output read, the layer output written)."""
     d, f, g = cfg.d, cfg.f, cfg.g
     idx = np.asarray(idx).ravel()
     bits = np.asarray(bits).ravel().astype(np.int64)
     be = np.zeros(cfg.E, dtype=np.int64)
     np.maximum.at(be, idx, bits)
     act = be > 0
-    planes = int(np.sum(be[act])) * 3 * d * f // 8
-    sz = int(np.sum(act)) * 3 * d * f // g * 8
     T = idx.size // cfg.k
-    io = T * d * 2 + T * d * 4 * (2 if accumulate else 1) + idx.size * f * 2 * 2
-    return planes + sz + io, float(np.mean(be[act])), float(np.mean(bits)), int(np.sum(act))
+    ns, fs = getattr(cfg, "n_shared", 0), getattr(cfg, "f_shared", 0)
+    planes13 = int(np.sum(be[act])) * 2 * d * f // 8 + ns * cfg.b_max * 2 * d * fs // 8
+    planes2 = int(np.sum(be[act])) * d * f // 8 + ns * cfg.b_max * d * fs // 8
+    sz13 = int(np.sum(act)) * 2 * d * f // g * 8 + ns * 2 * d * fs // g * 8
+    sz2 = int(np.sum(act)) * d * f // g * 8 + ns * d * fs // g * 8
+    x_in = T * d * 2
+    y_out = T * d * 4 * (2 if accumulate else 1)
+    h = (idx.size * f + ns * T * fs) * 2
+    w13 = planes13 + sz13 + x_in + h
+    w2 = planes2 + sz2 + h + y_out
+    return dict(total=w13 + w2, w13=w13, w2=w2, bits_read=float(np.mean(be[act])), bits_alloc=float(np.mean(bits)),
+                n_active=int(np.sum(act)))
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_qwen_T32_b3.0_hbm_bytes.md")
@@ -136,7 +154,13 @@ def router_bytes(cfg, T):
 
 
 class Layer:
-    """Device state for one workload: bank copies, x batches, buffers, graphs."""
+    """Device state for one workload: bank copies, x batches, buffers, graphs.
+
+    The per-pair widths of a step come from `policy`: "threshold" (the
+    gate-threshold bisection of the batch: one moe_layer call, or route +
+    alloc + FFN when timed with events), "calibrated" (a fixed threshold
+    tau), "duorate" (per-expert widths `expert_bits`) or "dpa" (residual-
+    aware chunk allocation over the residuals `resid`)."""
 
     def __init__(self, cfg, w, torch, bd, T):
         self.cfg, self.torch, self.bd, self.T = cfg, torch, bd, T
@@ -144,51 +168,69 @@ class Layer:
         dev = "cuda"
         base = bd.DeviceBank.from_host(w.routed)
         self.banks = [base] + [base.clone() for _ in range(N_COPIES - 1)]
+        self.shared = None
+        if w.shared is not None:
+            sb = bd.DeviceBank.from_host(w.shared)
+            self.shared = [sb] + [sb.clone() for _ in range(N_COPIES - 1)]
         from dynamic_any_precision_amd import workloads as wl
         self.xs = [bd.bf16_tensor(wl.step_activations(cfg, s, T)) for s in range(N_XBATCH)]
         self.wr = torch.from_numpy(w.w_router).to(dev)
         self.rws = bd.route_workspace(T, cfg.E)
-        self.fws = bd.ffn_workspace(base, None, T, cfg.k)
-        self.lws = bd.layer_workspace(base, None, T, cfg.k)
+        sh0 = self.shared[0] if self.shared else None
+        self.fws = bd.ffn_workspace(base, sh0, T, cfg.k)
+        self.lws = bd.layer_workspace(base, sh0, T, cfg.k)
         self.idx = [torch.empty(T, cfg.k, dtype=torch.int32, device=dev) for _ in range(N_XBATCH)]
         self.gate = [torch.empty(T, cfg.k, dtype=torch.float32, device=dev) for _ in range(N_XBATCH)]
         self.bits = [torch.empty(T * cfg.k, dtype=torch.uint8, device=dev) for _ in range(N_XBATCH)]
         self.y = torch.empty(T, cfg.d, dtype=torch.float32, device=dev)
         self.graphs = {}
-        self.tau = None  # calibration-threshold mode: fixed gate threshold (host float)
+        self.policy = "threshold"
+        self.tau = None          # calibrated: fixed gate threshold (host float)
+        self.expert_bits = None  # duorate: [E] uint8 device
+        self.resid = None        # dpa: [E][B] float64 device
+        self.dws = None          # dpa workspace
 
-    def step(self, i, target, ev=None):
-        """One layer step: moe_layer (one call), or with ev the three calls
-        route, alloc, FFN with HIP events around the FFN call."""
+    def widths(self, s, target):
+        bd, cfg = self.bd, self.cfg
+        if self.policy == "calibrated":
+            bd.bits_from_threshold(self.gate[s].view(-1), self.tau, cfg.b_lo, cfg.b_max, bits=self.bits[s])
+        elif self.policy == "duorate":
+            bd.bits_from_expert_widths(self.idx[s].view(-1), self.expert_bits, bits=self.bits[s])
+        elif self.policy == "dpa":
+            bd.dpa_alloc(self.gate[s].view(-1), self.idx[s].view(-1), self.resid, cfg.b_lo, cfg.b_max, target,
+                         bits=self.bits[s], workspace=self.dws)
+        else:
+            bd.alloc_bits(self.gate[s].view(-1), cfg.b_lo, cfg.b_max, target, bits=self.bits[s])
+
+    def step(self, i, target, ev=None, kev=None):
+        """One layer step: moe_layer (one call), or with ev the calls route,
+        widths, FFN with HIP events ev around the FFN call and kev (four
+        events) around its gate/up and down kernels."""
         bd, cfg = self.bd, self.cfg
         s = i % N_XBATCH
         bank = self.banks[i % N_COPIES]
-        if self.tau is not None:
-            # calibration-threshold mode: route, fixed-threshold widths, FFN
-            bd.route(self.xs[s], self.wr, self.bias, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
-            bd.bits_from_threshold(self.gate[s].view(-1), self.tau, cfg.b_lo, cfg.b_max, bits=self.bits[s])
-            if ev is not None:
-                ev[0].record()
-            bd.anyprec_ffn(bank, None, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
-                           workspace=self.fws)
-            if ev is not None:
-                ev[1].record()
-            return
-        if ev is None:
-            bd.layer(bank, None, self.xs[s], self.wr, self.bias, cfg.k, cfg.b_lo, target, y=self.y, idx=self.idx[s],
-                     gate=self.gate[s], bits=self.bits[s], workspace=self.lws)
+        shared = self.shared[i % N_COPIES] if self.shared else None
+        if self.policy == "threshold" and ev is None:
+            bd.layer(bank, shared, self.xs[s], self.wr, self.bias, cfg.k, cfg.b_lo, target, y=self.y,
+                     idx=self.idx[s], gate=self.gate[s], bits=self.bits[s], workspace=self.lws)
             return
         bd.route(self.xs[s], self.wr, self.bias, cfg.k, workspace=self.rws, idx=self.idx[s], gate=self.gate[s])
-        bd.alloc_bits(self.gate[s].view(-1), cfg.b_lo, cfg.b_max, target, bits=self.bits[s])
-        ev[0].record()
-        bd.anyprec_ffn(bank, None, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
+        self.widths(s, target)
+        if ev is not None:
+            ev[0].record()
+        if kev is not None:
+            bd.set_kernel_events(kev)
+        bd.anyprec_ffn(bank, shared, self.xs[s], self.idx[s], self.gate[s], self.bits[s], y=self.y,
                        workspace=self.fws)
-        ev[1].record()
+        if kev is not None:
+            bd.set_kernel_events(None)
+        if ev is not None:
+            ev[1].record()
 
     def capture(self, target, nsteps=N_XBATCH):
         """HIP graph of steps 0 .. nsteps-1 of a cycle (nsteps <= N_XBATCH)."""
         torch = self.torch
-        key = (float(target), nsteps)
+        key = (float(target), nsteps, self.policy)
         if key in self.graphs:
             return self.graphs[key]
         gs = []
@@ -226,60 +268,94 @@ class Layer:
         return (time.perf_counter() - t0) / steps
 
     def timed_events(self, target, steps):
-        """Eager steps; HIP events around each FFN call on the current stream."""
+        """Eager steps on the current stream: HIP events around each FFN call
+        and around its gate/up and down kernels (recorded by the library on
+        the call's stream)."""
         torch = self.torch
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(N_XBATCH)]
+
+        def evs(n):
+            out = []
+            for _ in range(n):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+                for x in e:
+                    x.record()            # creates the HIP event behind each
+                out.append(e)
+            return out
+        warm, run = evs(N_XBATCH), evs(steps)
+        torch.cuda.synchronize()
         for i in range(N_XBATCH):
-            self.step(i, target, warm[i])
+            self.step(i, target, warm[i][:2], warm[i][2:])
         torch.cuda.synchronize()
         for i in range(steps):
-            self.step(i, target, evs[i])
+            self.step(i, target, run[i][:2], run[i][2:])
         torch.cuda.synchronize()
-        ffn_ms = [a.elapsed_time(b) for a, b in evs]
-        nbytes, bread, balloc, nact = [], [], [], []
+        ffn_ms = [e[0].elapsed_time(e[1]) for e in run]
+        w13_ms = [e[2].elapsed_time(e[3]) for e in run]
+        w2_ms = [e[4].elapsed_time(e[5]) for e in run]
+        kb = []
         for i in range(steps):
             s = i % N_XBATCH
-            b, br, ba, na = algorithmic_ffn_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg)
-            nbytes.append(b); bread.append(br); balloc.append(ba); nact.append(na)
+            kb.append(kernel_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg))
         cfg = self.cfg
         flops = 6.0 * cfg.d * cfg.f * self.T * cfg.k  # routed SwiGLU FFN: gate, up, down
+
+        def mean(key):
+            return float(np.mean([k[key] for k in kb]))
         return dict(ffn_ms=float(np.mean(ffn_ms)), ffn_ms_p10=float(np.percentile(ffn_ms, 10)), ffn_flops=flops,
                     ffn_ms_p50=float(np.percentile(ffn_ms, 50)), ffn_ms_p90=float(np.percentile(ffn_ms, 90)),
-                    ffn_bytes=float(np.mean(nbytes)), bits_read=float(np.mean(bread)),
-                    bits_alloc=float(np.mean(balloc)), n_active=float(np.mean(nact)))
+                    w13_ms=float(np.mean(w13_ms)), w2_ms=float(np.mean(w2_ms)),
+                    ffn_bytes=mean("total"), w13_bytes=mean("w13"), w2_bytes=mean("w2"), bits_read=mean("bits_read"),
+                    bits_alloc=mean("bits_alloc"), n_active=mean("n_active"))
 
 
-def cpu_baseline(cfg, w, budget_s=20.0):
+def kernel_roofline(ev, traffic=None):
+    """Roofline of the dominant kernel (gate/up): its algorithmic bytes per
+    launch over its event-timed duration, against the 8 TB/s HBM peak; the
+    down kernel and the whole FFN call beside it."""
+    a13 = ev["w13_bytes"] / (ev["w13_ms"] * 1e-3) / 1e9
+    a2 = ev["w2_bytes"] / (ev["w2_ms"] * 1e-3) / 1e9
+    ac = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": a13, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a13 / HBM_PEAK_GBS,
+            "traffic": traffic, "kernel": "k_ffn_ks gate/up + SwiGLU (moe_anyprec_ffn's dominant kernel)",
+            "bytes_per_launch": ev["w13_bytes"], "us_per_launch": ev["w13_ms"] * 1e3,
+            "down_kernel": {"achieved": a2, "frac": a2 / HBM_PEAK_GBS, "bytes_per_launch": ev["w2_bytes"],
+                            "us_per_launch": ev["w2_ms"] * 1e3},
+            "ffn_call": {"achieved": ac, "frac": ac / HBM_PEAK_GBS, "bytes_per_launch": ev["ffn_bytes"],
+                         "us_per_launch": ev["ffn_ms"] * 1e3,
+                         "kernels": "plan, activation gather, gate/up + SwiGLU, down, combine"}}
+
+
+def cpu_baseline(cfg, w, budget_s=10.0):
     """The oracle, untouched, on a bounded sample: whole routing and
-    allocation of one T-token batch plus the expert FFN of its first tokens,
-    in one host thread."""
+    allocation of one T-token batch plus the expert FFN (routed and shared)
+    of its first tokens, each token on a fresh dequantisation cache.  Timed
+    with NumPy's BLAS on every core this process may use, then on one core."""
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    done_tokens = 0
-    t0 = time.perf_counter()
-    try:
-        if ctx:
-            ctx.__enter__()
-        rc = orc.bank_cache(w.routed)          # fresh cache: dequantisation is part of the work
-        tok = 0
-        while time.perf_counter() - t0 < budget_s and tok < cfg.T:
-            orc.layer(w.x_bf16, w.w_router, None, cfg.k, cfg.b_lo, cfg.b_max, cfg.target, rc, tokens=[tok])
-            rc = orc.bank_cache(w.routed)
-            tok += 1
-            done_tokens += 1
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    el = time.perf_counter() - t0
-    return dict(value=done_tokens / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done_tokens} token(s) of the T={cfg.T} batch: full routing and allocation of the batch "
-                       f"plus those tokens' 8 expert FFNs (dequantised from the stored planes), float64 NumPy, "
-                       f"{el:.1f} s")
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+
+    def run(limit):
+        done = 0
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=limit):
+            tok = 0
+            while time.perf_counter() - t0 < budget_s and tok < cfg.T:
+                rc = orc.bank_cache(w.routed)          # dequantisation is part of the work
+                sc = orc.bank_cache(w.shared) if w.shared is not None else None
+                orc.layer(w.x_bf16, w.w_router, w.logit_bias, cfg.k, cfg.b_lo, cfg.b_max, cfg.target, rc, sc,
+                          cfg.n_shared, tokens=[tok])
+                tok += 1
+                done += 1
+        return done, time.perf_counter() - t0
+    n_all, t_all = run(cores)
+    n_one, t_one = run(1)
+    what = (f"token(s) of the T={cfg.T} batch: full routing and allocation of the batch plus those tokens' "
+            f"{cfg.k} routed expert FFNs" + (f" and {cfg.n_shared} shared" if cfg.n_shared else "") +
+            " (dequantised from the stored planes), float64 NumPy")
+    return dict(value=n_all / t_all, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n_all} {what}, {t_all:.1f} s on {cores} cores",
+                single_core={"value": n_one / t_one, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{n_one} {what}, {t_one:.1f} s on 1 core"})
 
 
 def main():
@@ -293,6 +369,12 @@ def main():
                     help="a decode step through the 48-layer stack (T=64) instead of the single-layer headline")
     ap.add_argument("--calibrated", action="store_true",
                     help="calibration-threshold mode: a gate threshold fixed from calibration batches")
+    ap.add_argument("--deepseek", action="store_true",
+                    help="the DeepSeekMoE-16B-shaped decode layer (T=16, two shared experts, B_lo 2 and 1)")
+    ap.add_argument("--duorate", action="store_true",
+                    help="DuoRate per-expert widths solved on a prefill profile, then decode steps at those widths")
+    ap.add_argument("--dpa", action="store_true",
+                    help="DPA-MoE residual-aware chunk allocation over widths 1-4 on every decode step")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--target", type=float, default=3.0)
@@ -332,6 +414,10 @@ def main():
         return stack(args, torch, bd, wl)
     if args.calibrated:
         return calibrated(args, torch, bd, wl)
+    if args.deepseek:
+        return deepseek(args, torch, bd, wl)
+    if args.duorate or args.dpa:
+        return per_expert_modes(args, torch, bd, wl)
     cfg = wl.config(2, T=args.tokens, target=args.target)
     log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
     t0 = time.perf_counter()
@@ -351,8 +437,9 @@ def main():
     t_step = L.timed_graph(args.target, args.steps, args.warmup)
     log(f"step {t_step * 1e3:.4f} ms; event-timing the FFN stage")
     ev = L.timed_events(args.target, args.steps)
-    achieved = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
     step_bytes = ev["ffn_bytes"] + router_bytes(cfg, T)
+    log(f"gate/up {ev['w13_ms'] * 1e3:.1f} us ({ev['w13_bytes'] / ev['w13_ms'] / 1e6:.0f} GB/s), down "
+        f"{ev['w2_ms'] * 1e3:.1f} us, FFN call {ev['ffn_ms'] * 1e3:.1f} us")
 
     sweep = []
     if not args.no_sweep:
@@ -363,12 +450,15 @@ def main():
                 ts = LT.timed_graph(tgt, n, 5)
                 e2 = LT.timed_events(tgt, n)
                 gbs = e2["ffn_bytes"] / (e2["ffn_ms"] * 1e-3) / 1e9
+                g13 = e2["w13_bytes"] / (e2["w13_ms"] * 1e-3) / 1e9
                 sweep.append(dict(T=TT, target=tgt, tokens_per_s=TT / ts, ms_per_step=ts * 1e3,
                                   ffn_ms=e2["ffn_ms"], ffn_gbs=gbs, ffn_frac=gbs / HBM_PEAK_GBS,
-                                  bits_read=e2["bits_read"], bits_alloc=e2["bits_alloc"],
+                                  w13_us=e2["w13_ms"] * 1e3, w13_gbs=g13, w13_frac=g13 / HBM_PEAK_GBS,
+                                  w2_us=e2["w2_ms"] * 1e3, bits_read=e2["bits_read"], bits_alloc=e2["bits_alloc"],
                                   n_active=e2["n_active"], ffn_bytes=e2["ffn_bytes"]))
                 log(f"sweep T={TT} target={tgt}: {TT / ts:.0f} tok/s, FFN {e2['ffn_ms'] * 1e3:.1f} us, "
-                    f"{gbs:.0f} GB/s, bits read {e2['bits_read']:.2f}")
+                    f"{gbs:.0f} GB/s; gate/up {e2['w13_ms'] * 1e3:.1f} us {g13:.0f} GB/s; bits read "
+                    f"{e2['bits_read']:.2f}")
 
     ceiling = read_ceiling(torch, bd)
     log(f"streaming-read ceiling {ceiling:.0f} GB/s")
@@ -400,11 +490,8 @@ def main():
         "bits_alloc": ev["bits_alloc"],
         "n_active_experts": ev["n_active"],
         "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(T, args.target),
-                     "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling,
-                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
-                     "bytes_per_launch": ev["ffn_bytes"]},
+        "roofline": dict(kernel_roofline(ev, recorded_traffic(T, args.target)), read_ceiling=ceiling,
+                         frac_of_read_ceiling=ev["w13_bytes"] / (ev["w13_ms"] * 1e-3) / 1e9 / ceiling),
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
@@ -453,6 +540,138 @@ def prefill(args, torch, bd, wl):
     print(json.dumps(out), flush=True)
 
 
+def deepseek(args, torch, bd, wl):
+    """The DeepSeekMoE-16B-shaped decode layer: T=16, 64 routed experts of
+    intermediate 1408, top-6, two always-on shared experts read at 4 bits,
+    target 2.5 bits, B_lo 2 (the headline) and 1."""
+    rows, head = [], None
+    for b_lo in (2, 1):
+        cfg = wl.config(3, b_lo=b_lo, target=2.5 if args.target == 3.0 else args.target)
+        T = cfg.T
+        log(f"generating the DeepSeekMoE-16B-shaped layer (seeded), B_lo {b_lo}")
+        w = wl.make_workload(cfg, keep_codes=False)
+        L = Layer(cfg, w, torch, bd, T)
+        ts = L.timed_graph(cfg.target, args.steps, args.warmup)
+        ev = L.timed_events(cfg.target, args.steps)
+        g13 = ev["w13_bytes"] / (ev["w13_ms"] * 1e-3) / 1e9
+        row = dict(b_lo=b_lo, target=cfg.target, tokens_per_s=T / ts, ms_per_step=ts * 1e3,
+                   ffn_us=ev["ffn_ms"] * 1e3, w13_us=ev["w13_ms"] * 1e3, w13_gbs=g13, w13_frac=g13 / HBM_PEAK_GBS,
+                   w2_us=ev["w2_ms"] * 1e3, bits_read=ev["bits_read"], bits_alloc=ev["bits_alloc"],
+                   n_active=ev["n_active"], ffn_bytes=ev["ffn_bytes"])
+        rows.append(row)
+        log(f"deepseek B_lo={b_lo}: {T / ts:.0f} tok/s, FFN {ev['ffn_ms'] * 1e3:.1f} us, gate/up "
+            f"{ev['w13_ms'] * 1e3:.1f} us ({g13:.0f} GB/s), bits read {ev['bits_read']:.2f}")
+        if head is None:
+            head = (cfg, w, ts, ev)
+        del L
+        torch.cuda.empty_cache()
+    cfg, w, ts, ev = head
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, w)
+    out = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s vs avg bits read (DeepSeekMoE-16B shape)",
+        "value": cfg.T / ts, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ts * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DeepSeekMoE-16B-shaped single MoE layer, decode, two shared experts",
+                   "tokens": cfg.T, "hidden": cfg.d, "expert_intermediate": cfg.f, "experts": cfg.E,
+                   "top_k": cfg.k, "shared_experts": cfg.n_shared, "bitplanes": cfg.b_max, "group": cfg.g,
+                   "b_lo": cfg.b_lo, "target_avg_bits": cfg.target, "weight_copies_rotated": N_COPIES,
+                   "activation_batches": N_XBATCH},
+        "bits_read": ev["bits_read"], "bits_alloc": ev["bits_alloc"], "n_active_experts": ev["n_active"],
+        "roofline": kernel_roofline(ev),
+        "cpu_baseline": cpu,
+        "sweep": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def per_expert_modes(args, torch, bd, wl):
+    """The Qwen3-30B-A3B-shaped decode layer (T=32) with widths from DuoRate's
+    per-expert solve (--duorate: the distortion tensor baked from the bank,
+    a 4096-token prefill of fresh activations profiled through the router,
+    widths 1..4 per expert, decode steps reading each pair at its expert's
+    width) or from DPA-MoE's residual-aware chunk allocation on every step
+    (--dpa: widths 1..4 per pair)."""
+    mode = "duorate" if args.duorate else "dpa"
+    cfg = wl.config(2, T=args.tokens, b_lo=1, target=args.target)
+    T = cfg.T
+    log(f"generating the Qwen3-30B-A3B-shaped layer (seeded); {mode} widths")
+    w = wl.make_workload(cfg, keep_codes=False)
+    L = Layer(cfg, w, torch, bd, T)
+    L.policy = mode
+    extra = {}
+    if mode == "duorate":
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        delta = bd.duorate_bake(L.banks[0])
+        torch.cuda.synchronize()
+        t_bake = time.perf_counter() - t0
+        xp = bd.bf16_tensor(wl.step_activations(cfg, 50_000, 4096))
+        idx_p, _ = bd.route(xp, L.wr, None, cfg.k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a, n = bd.duorate_profile(xp, idx_p, cfg.E)
+        torch.cuda.synchronize()
+        t_prof = time.perf_counter() - t0
+        n_np = n.cpu().numpy().astype(np.int64)
+        extra = {"bake_ms": t_bake * 1e3, "profile_ms": t_prof * 1e3, "prefill_tokens": 4096}
+    else:
+        L.resid = bd.dpa_residuals(L.banks[0])
+        L.dws = torch.empty(max(256, int(bd.lib().moe_dpa_alloc_workspace_bytes(T * cfg.k, cfg.b_lo, cfg.b_max))),
+                            dtype=torch.uint8, device="cuda")
+    stored_bpw = cfg.b_max + 64.0 / cfg.g   # the uniform stored tier plus fp32 (scale, zero) per group
+    rows, head = [], None
+    targets = sorted({1.75, 2.0, 2.3, 2.5, 2.9, 3.0, 3.5, args.target})
+    for tgt in targets:
+        if mode == "duorate":
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            wts, D, lam = bd.duorate_solve(delta, a, n, cfg.b_lo, cfg.b_max, tgt)
+            torch.cuda.synchronize()
+            t_solve = time.perf_counter() - t0
+            L.expert_bits = wts
+            wn = wts.cpu().numpy().astype(np.int64)
+            prof_rate = float(np.dot(n_np, wn)) / max(1, int(n_np.sum()))
+        ts = L.timed_graph(tgt, args.steps, args.warmup)
+        ev = L.timed_events(tgt, args.steps)
+        g13 = ev["w13_bytes"] / (ev["w13_ms"] * 1e-3) / 1e9
+        row = dict(target=tgt, tokens_per_s=T / ts, ms_per_step=ts * 1e3, ffn_us=ev["ffn_ms"] * 1e3,
+                   w13_us=ev["w13_ms"] * 1e3, w13_gbs=g13, w13_frac=g13 / HBM_PEAK_GBS, w2_us=ev["w2_ms"] * 1e3,
+                   bits_read=ev["bits_read"], bits_alloc=ev["bits_alloc"], n_active=ev["n_active"],
+                   stored_bpw=stored_bpw, read_bpw=ev["bits_read"] + 64.0 / cfg.g)
+        if mode == "duorate":
+            row.update(solve_ms=t_solve * 1e3, lam=float(lam.item()), profile_rate=prof_rate,
+                       expert_widths=np.bincount(wn, minlength=cfg.b_max + 1)[1:].tolist())
+        rows.append(row)
+        log(f"{mode} target={tgt}: {T / ts:.0f} tok/s, gate/up {ev['w13_ms'] * 1e3:.1f} us ({g13:.0f} GB/s), "
+            f"bits read {ev['bits_read']:.2f}, allocated {ev['bits_alloc']:.2f}")
+        if tgt == args.target:
+            head = (ts, ev, row)
+    ts, ev, row = head
+    name = "DuoRate per-expert widths" if mode == "duorate" else "DPA-MoE residual-aware chunk allocation"
+    out = {
+        "metric": f"MoE-layer tokens/s, {name} (Qwen3-30B shape)",
+        "value": T / ts, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ts * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"Qwen3-30B-A3B-shaped single MoE layer, decode, {name}", "tokens": T,
+                   "hidden": cfg.d, "expert_intermediate": cfg.f, "experts": cfg.E, "top_k": cfg.k,
+                   "bitplanes": cfg.b_max, "group": cfg.g, "widths": [cfg.b_lo, cfg.b_max],
+                   "target_rate_bits": args.target, "weight_copies_rotated": N_COPIES,
+                   "activation_batches": N_XBATCH},
+        "bits_read": ev["bits_read"], "bits_alloc": ev["bits_alloc"], "stored_bpw": stored_bpw,
+        "read_bpw": row["read_bpw"],
+        "roofline": kernel_roofline(ev),
+        "cpu_baseline": None,
+        "sweep": rows,
+        **extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
 N_CAL = 64  # calibration batches (and as many held-out batches)
 
 
@@ -478,6 +697,7 @@ def calibrated(args, torch, bd, wl):
         tau = float(tau_t.item())
         hb = bd.bits_from_threshold(held, tau, cfg.b_lo, cfg.b_max).view(N_CAL, T * cfg.k).float().mean(1).cpu().numpy()
         L.tau = tau
+        L.policy = "calibrated"
         ts = L.timed_graph(tgt, args.steps, args.warmup)
         ev = L.timed_events(tgt, args.steps)
         row = dict(target=tgt, tau=tau, tokens_per_s=T / ts, ms_per_step=ts * 1e3, ffn_ms=ev["ffn_ms"],
@@ -490,7 +710,6 @@ def calibrated(args, torch, bd, wl):
         if tgt == args.target:
             head = (ts, ev, row)
     ts, ev, row = head
-    achieved = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
     out = {
         "metric": "MoE-layer tokens/s, calibration-threshold mode (Qwen3-30B shape)",
         "value": T / ts,
@@ -513,10 +732,7 @@ def calibrated(args, torch, bd, wl):
         "held_out_bits": row["held_out_bits"],
         "bits_read": ev["bits_read"],
         "bits_alloc": ev["bits_alloc"],
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
-                     "bytes_per_launch": ev["ffn_bytes"]},
+        "roofline": kernel_roofline(ev),
         "cpu_baseline": None,
         "sweep": rows,
     }

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "moe_dpa_alloc": (i32, [vp, vp, i32, vp, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
             "moe_status_string": (ctypes.c_char_p, [i32]),
             "moe_last_hip_error": (i32, []),
+            "moe_set_kernel_events": (None, [vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -430,6 +431,17 @@ def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=N
     st = lib().moe_stream_read(_ptr(buf, name="buf"), nbytes, sink.data_ptr(), _stream(stream))
     _check(st, "moe_stream_read")
     return sink
+
+
+def set_kernel_events(events=None):
+    """Record four torch.cuda.Event objects (gate/up begin, end; down begin,
+    end) around the FFN's streaming kernels of the following calls on this
+    thread; None turns the marks off.  Each event must have been recorded
+    once before (so that its HIP event exists)."""
+    if events is None:
+        lib().moe_set_kernel_events(None, None, None, None)
+    else:
+        lib().moe_set_kernel_events(*[ev.cuda_event for ev in events])
 
 
 def bf16_tensor(bits_u16: np.ndarray, device="cuda") -> torch.Tensor:

@@ -104,6 +104,13 @@ moe_status ffn_shape(const moe_expert_bank* routed, const moe_expert_bank* share
   return MOE_OK;
 }
 
+// Measurement hook: events recorded around the gate/up and down kernels.
+thread_local hipEvent_t g_kernel_events[4] = {nullptr, nullptr, nullptr, nullptr};
+
+hipError_t mark(int i, hipStream_t strm) {
+  return g_kernel_events[i] ? hipEventRecord(g_kernel_events[i], strm) : hipSuccess;
+}
+
 // The FFN after the plan: activation gather, gate/up + SwiGLU, down, combine.
 hipError_t ffn_after_plan(const moe::FfnShape& s, const moe::FfnLayout& L, char* ws, const moe_expert_bank* routed,
                           const moe_expert_bank* shared, const uint16_t* x, const float* topk_gate, float* y,
@@ -114,9 +121,13 @@ hipError_t ffn_after_plan(const moe::FfnShape& s, const moe::FfnLayout& L, char*
   none.N = 16;
   none.K = 128;
   hipError_t e = moe::launch_gather(s, L, ws, x, strm);
+  if (e == hipSuccess) e = mark(0, strm);
   if (e == hipSuccess)
     e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = mark(1, strm);
+  if (e == hipSuccess) e = mark(2, strm);
   if (e == hipSuccess) e = moe::launch_ffn_w2(s, L, ws, w2_of(routed), shared ? w2_of(shared) : none, ncu, strm);
+  if (e == hipSuccess) e = mark(3, strm);
   if (e == hipSuccess) e = moe::launch_combine(s, L, ws, topk_gate, y, accumulate, strm);
   return e;
 }
@@ -124,6 +135,7 @@ hipError_t ffn_after_plan(const moe::FfnShape& s, const moe::FfnLayout& L, char*
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
+
 
 extern "C" {
 
@@ -142,6 +154,13 @@ const char* moe_status_string(moe_status s) {
 }
 
 int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+void moe_set_kernel_events(void* w13_begin, void* w13_end, void* w2_begin, void* w2_end) {
+  g_kernel_events[0] = static_cast<hipEvent_t>(w13_begin);
+  g_kernel_events[1] = static_cast<hipEvent_t>(w13_end);
+  g_kernel_events[2] = static_cast<hipEvent_t>(w2_begin);
+  g_kernel_events[3] = static_cast<hipEvent_t>(w2_end);
+}
 
 size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
   if (T < 0 || E < 1) return 0;

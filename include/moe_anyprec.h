@@ -430,6 +430,17 @@ moe_status moe_rmsnorm_to_bf16(const float* h, uint16_t* x, int32_t rows, int32_
 #define MOE_STREAM_SINK 8192
 moe_status moe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Measurement hook for callers that time the two streaming kernels of the
+ * FFN stage on their own (the roofline of the dominant kernel): while set,
+ * every moe_anyprec_ffn and moe_layer call on this host thread records
+ * w13_begin / w13_end on its stream right before / after the gate/up kernel,
+ * and w2_begin / w2_end around the down kernel.  Arguments are hipEvent_t
+ * handles (created and owned by the caller) passed as void*; NULL disables
+ * that mark.  All NULL is the default.  Thread-local; no other effect.
+ */
+void moe_set_kernel_events(void* w13_begin, void* w13_end, void* w2_begin, void* w2_end);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status status);
 
