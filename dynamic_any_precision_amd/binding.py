@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer_workspace_bytes": (sz, [bp, bp, i32, i32]),
             "moe_layer": (i32, [bp, bp, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp, sz, vp]),
             "moe_dequant": (i32, [bp, i32, i32, i32, vp, vp]),
+            "moe_layer_static_scratch_bytes": (sz, []),
+            "moe_layer_static": (i32, [bp, bp, vp, i32, i32, vp, vp, i32, i32, f32, vp, vp, vp, vp, i32, vp]),
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
             "moe_rmsnorm_to_bf16": (i32, [vp, vp, i32, i32, f32, vp]),
             "moe_bits_from_threshold": (i32, [vp, i32, f32, i32, i32, vp, vp]),
@@ -291,6 +293,31 @@ def layer(routed: DeviceBank, shared: Optional[DeviceBank], x: torch.Tensor, w_r
                          _ptr(y, torch.float32, "y"), int(accumulate), _ptr(workspace, name="workspace"),
                          workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_layer")
+    return y, idx, gate, bits
+
+
+def layer_static(routed: DeviceBank, shared: Optional[DeviceBank], x: torch.Tensor, w_router: torch.Tensor,
+                 logit_bias: Optional[torch.Tensor], top_k: int, b_lo: int, target: float, renorm: bool = False,
+                 y: Optional[torch.Tensor] = None, accumulate: bool = False, idx: Optional[torch.Tensor] = None,
+                 gate: Optional[torch.Tensor] = None, bits: Optional[torch.Tensor] = None, stream=None):
+    """moe_layer on the library's static scratch array (no workspace); returns y, idx, gate, bits."""
+    T, d = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.zeros(T, d, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    if gate is None:
+        gate = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+    if bits is None:
+        bits = torch.empty(T * top_k, dtype=torch.uint8, device=dev)
+    st = lib().moe_layer_static(ctypes.byref(routed.struct()), _bank_struct(shared), _ptr(x, _BF16, "x"), T, top_k,
+                                _ptr(w_router, torch.float32, "w_router"),
+                                _ptr(logit_bias, torch.float32, "logit_bias"), int(renorm), b_lo, float(target),
+                                _ptr(idx, torch.int32, "topk_idx"), _ptr(gate, torch.float32, "topk_gate"),
+                                _ptr(bits, torch.uint8, "bits"), _ptr(y, torch.float32, "y"), int(accumulate),
+                                _stream(stream))
+    _check(st, "moe_layer_static")
     return y, idx, gate, bits
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_anyprec.so")
 
-SOURCES = ["route.hip", "alloc.hip", "permute.hip", "control.hip", "ffn.hip", "dequant.hip", "duorate.hip", "dpa.hip", "api.cpp"]
+SOURCES = ["route.hip", "alloc.hip", "permute.hip", "control.hip", "ffn.hip", "dequant.hip", "duorate.hip", "dpa.hip", "noalloc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -136,6 +136,13 @@ size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
 
+namespace moe {
+int record_hip_error(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+}  // namespace moe
+
 
 extern "C" {
 

@@ -7,6 +7,9 @@
 
 namespace moe {
 
+// Record a HIP error for moe_last_hip_error() on this thread; returns MOE_ERR_HIP (7).
+int record_hip_error(hipError_t e);
+
 // ---- router
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const uint16_t* x, int T, int d, const float* W, int E, const float* bias, int k,

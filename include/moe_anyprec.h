@@ -246,6 +246,26 @@ moe_status moe_layer(const moe_expert_bank* routed, const moe_expert_bank* share
                      float* y, int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as moe_layer, without the workspace: the
+ * call uses a static device array of the library (its size is
+ * moe_layer_static_scratch_bytes(), 64 MiB, enough for decode batches of up
+ * to 256 tokens on the Qwen3-30B-A3B shape), and calls no allocating
+ * routine.  A call whose moe_layer_workspace_bytes exceeds that size returns
+ * MOE_ERR_WORKSPACE.  Each GPU holds one such array until the process ends,
+ * shared by every call on that GPU and keeping the last call's contents:
+ * no part of it needs to start at zero (every call writes what it reads),
+ * but calls that overlap in time on one GPU (on different streams or host
+ * threads) race on it and must be ordered by the caller.
+ */
+size_t moe_layer_static_scratch_bytes(void);
+moe_status moe_layer_static(const moe_expert_bank* routed, const moe_expert_bank* shared, const uint16_t* x,
+                            int32_t T, int32_t top_k, const float* w_router, const float* logit_bias,
+                            int32_t renorm_topk, int32_t b_lo, float target_avg_bits, int32_t* topk_idx,
+                            float* topk_gate, uint8_t* bits, float* y, int32_t accumulate, void* stream);
+
+/*
  * The token-to-expert permutation and histogram step of moe_anyprec_ffn, on
  * its own, for inspection.  Pairs are ordered stably by (expert ascending,
  * bits descending, pair id ascending), pair id = t*top_k + j.
