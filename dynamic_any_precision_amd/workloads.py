@@ -60,6 +60,7 @@ class MoeConfig:
     n_shared: int = 0             # always-on shared experts (read at b_max)
     f_shared: int = 0
     renorm_topk: bool = False
+    ragged: bool = False          # per-expert maximum width B_e in {2, 3, 4} (ragged plane counts)
 
     @property
     def P(self) -> int:
@@ -270,6 +271,78 @@ def make_workload(cfg: MoeConfig, keep_codes: bool = True, T: Optional[int] = No
         if keep_codes:
             shared.q13, shared.q2, shared.s13, shared.z13, shared.s2, shared.z2 = sq13, sq2, ss13, sz13, ss2, sz2
     return Workload(cfg, x, w_router, logit_bias, routed, shared)
+
+
+@dataclasses.dataclass
+class RaggedBank:
+    """Encoded bank whose expert e stores its own number of planes B_e
+    (plane_prefix[e+1] - plane_prefix[e]): the planes of every expert are one
+    array of planes (uint32 [sum B_e, words]), expert e's in rows
+    plane_prefix[e] .. plane_prefix[e+1]-1, its codes B_e-bit and its
+    (scale, zero) those of B_e-bit quantisation; b_max is the largest B_e."""
+    n_experts: int
+    d: int
+    f: int
+    g: int
+    b_max: int
+    plane_prefix: np.ndarray  # int32 [E+1]
+    w13_planes: np.ndarray    # uint32 [sum B_e, 2f/16 * 16 d/32]
+    w13_sz: np.ndarray        # float32 [E, 2f/16, d/g, 2, 16]
+    w2_planes: np.ndarray     # uint32 [sum B_e, d/16 * 16 f/32]
+    w2_sz: np.ndarray         # float32 [E, d/16, f/g, 2, 16]
+    q13: Optional[list] = None
+    q2: Optional[list] = None
+
+    def stored_bytes(self) -> int:
+        return (self.w13_planes.nbytes + self.w13_sz.nbytes + self.w2_planes.nbytes + self.w2_sz.nbytes)
+
+
+def expert_max_widths(cfg: MoeConfig) -> np.ndarray:
+    """Seeded per-expert maximum widths B_e in {2, 3, 4} (a quarter at 2,
+    a third at 3, the rest at 4), standing in for the offline choice under a
+    memory budget (stream SeedSequence([seed, 77]))."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 77])))
+    u = rng.random(cfg.E)
+    return np.where(u < 0.25, 2, np.where(u < 0.25 + 1 / 3, 3, 4)).astype(np.int32)
+
+
+def make_ragged_workload(cfg: MoeConfig, keep_codes: bool = True, widths: Optional[np.ndarray] = None) -> Workload:
+    """The workload of `cfg` with a ragged routed bank: the same seeded
+    weights as make_workload, expert e quantised to B_e bits
+    (expert_max_widths, or `widths`) and stored as B_e planes."""
+    st = _streams(cfg.seed)
+    d, f, E, g = cfg.d, cfg.f, cfg.E, cfg.g
+    # router and activations exactly as make_workload draws them
+    w_router = st["router"].standard_normal((E, d), dtype=np.float32) * np.float32(0.02)
+    if cfg.router_lognorm > 0:
+        rowscale = np.exp(st["lognorm"].normal(0.0, cfg.router_lognorm, size=E)).astype(np.float32)
+        w_router = (w_router * rowscale[:, None]).astype(np.float32)
+    x = f32_to_bf16_bits(st["x"].standard_normal((cfg.T, d), dtype=np.float32))
+    widths = expert_max_widths(cfg) if widths is None else np.asarray(widths, dtype=np.int32)
+    p13, p2, s13l, s2l, q13l, q2l = [], [], [], [], [], []
+    # redraw the same N(0, 0.02) weights expert by expert (streams w13 and w2 in order)
+    for e in range(E):
+        w13 = st["w13"].standard_normal((2 * f, d), dtype=np.float32) * np.float32(0.02)
+        q, s_, z = quantize_rtn(w13, g, int(widths[e]))
+        p13.append(pack_planes(q[None], int(widths[e]))[0])
+        s13l.append((s_, z))
+        if keep_codes:
+            q13l.append(q)
+    for e in range(E):
+        w2 = st["w2"].standard_normal((d, f), dtype=np.float32) * np.float32(0.02)
+        q, s_, z = quantize_rtn(w2, g, int(widths[e]))
+        p2.append(pack_planes(q[None], int(widths[e]))[0])
+        s2l.append((s_, z))
+        if keep_codes:
+            q2l.append(q)
+    prefix = np.concatenate([[0], np.cumsum(widths)]).astype(np.int32)
+    sz13 = pack_scale_zero(np.stack([a for a, _ in s13l]), np.stack([b for _, b in s13l]))
+    sz2 = pack_scale_zero(np.stack([a for a, _ in s2l]), np.stack([b for _, b in s2l]))
+    bank = RaggedBank(E, d, f, g, int(widths.max()), prefix, np.ascontiguousarray(np.concatenate(p13)), sz13,
+                      np.ascontiguousarray(np.concatenate(p2)), sz2)
+    if keep_codes:
+        bank.q13, bank.q2 = q13l, q2l
+    return Workload(cfg, x, w_router, None, bank, None)
 
 
 def step_activations(cfg: MoeConfig, step: int, T: Optional[int] = None) -> np.ndarray:

@@ -545,3 +545,53 @@ def dpa_allocate(gates: np.ndarray, idx: np.ndarray, resid: np.ndarray, b_lo: in
         chosen = flat > srt[n]
     bits = b_lo + chosen.reshape(s.shape).sum(axis=1)
     return bits.astype(np.int64), int(chosen.sum()), budget
+
+
+# ---------------------------------------------------------------------------
+# per-expert maximum width (ragged plane counts)
+
+
+class RaggedDequantCache(DequantCache):
+    """Dequantised matrices of a bank whose expert e stores its own number
+    of planes B_e = prefix[e+1] - prefix[e] (MatMoE review, Core
+    Contribution: each expert's maximum bit-width is chosen offline under a
+    memory budget; the choice itself is not made here).  The planes of all
+    experts are one array of planes, expert e's at rows prefix[e] ..
+    prefix[e+1]-1; the codes of expert e are B_e-bit and its (s, z) belong to
+    that precision.  A pair of width b reads min(b, B_e) planes (reading: an
+    expert can not be read wider than it is stored), with floor and
+    compensation relative to B_e."""
+
+    def __init__(self, planes13, sz13, planes2, sz2, prefix, d: int, f: int, g: int):
+        self.prefix = [int(v) for v in prefix]
+        super().__init__(planes13, sz13, planes2, sz2, d, f, g, max(
+            self.prefix[e + 1] - self.prefix[e] for e in range(len(self.prefix) - 1)))
+
+    def b_of(self, e: int) -> int:
+        return self.prefix[e + 1] - self.prefix[e]
+
+    def codes(self, e: int):
+        if e not in self._q:
+            d, f, g = self.d, self.f, self.g
+            Be = self.b_of(e)
+            p0, p1 = self.prefix[e], self.prefix[e + 1]
+            q13 = unpack_codes(np.asarray(self.p13)[None, p0:p1], Be, 2 * f, d)[0]
+            q2 = unpack_codes(np.asarray(self.p2)[None, p0:p1], Be, d, f)[0]
+            s13, z13 = unpack_scale_zero(self.sz13[e:e + 1], 2 * f, d // g)
+            s2, z2 = unpack_scale_zero(self.sz2[e:e + 1], d, f // g)
+            self._q[e] = (q13, s13[0], z13[0], q2, s2[0], z2[0])
+        return self._q[e]
+
+    def weights(self, e: int, b: int):
+        Be = self.b_of(e)
+        b = min(int(b), Be)
+        key = (e, b)
+        if key not in self._w:
+            q13, s13, z13, q2, s2, z2 = self.codes(e)
+            self._w[key] = (dequant(q13, s13, z13, b, Be, self.g), dequant(q2, s2, z2, b, Be, self.g))
+        return self._w[key]
+
+
+def ragged_bank_cache(bank) -> RaggedDequantCache:
+    return RaggedDequantCache(bank.w13_planes, bank.w13_sz, bank.w2_planes, bank.w2_sz, bank.plane_prefix,
+                              bank.d, bank.f, bank.g)
