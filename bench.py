@@ -74,14 +74,17 @@ def algorithmic_ffn_bytes(idx, bits, cfg, accumulate=False):
     return k["total"], k["bits_read"], k["bits_alloc"], k["n_active"]
 
 
-def kernel_bytes(idx, bits, cfg, accumulate=False):
+def kernel_bytes(idx, bits, cfg, accumulate=False, expert_widths=None):
     """Algorithmic bytes of the FFN stage and of its two streaming kernels:
     gate/up (W13 planes and (scale, zero) of the active experts, the shared
     experts' W13, the activations in, the SwiGLU output written) and down
-    (W2 likewise, the SwiGLU output read, the layer output written)."""
+    (W2 likewise, the SwiGLU output read, the layer output written).  With
+    per-expert stored widths (a ragged bank) a pair reads min(b, B_e)."""
     d, f, g = cfg.d, cfg.f, cfg.g
     idx = np.asarray(idx).ravel()
     bits = np.asarray(bits).ravel().astype(np.int64)
+    if expert_widths is not None:
+        bits = np.minimum(bits, np.asarray(expert_widths)[idx])
     be = np.zeros(cfg.E, dtype=np.int64)
     np.maximum.at(be, idx, bits)
     act = be > 0
@@ -189,6 +192,8 @@ class Layer:
         self.expert_bits = None  # duorate: [E] uint8 device
         self.resid = None        # dpa: [E][B] float64 device
         self.dws = None          # dpa workspace
+        pp = getattr(w.routed, "plane_prefix", None)
+        self.expert_widths = None if pp is None else np.diff(np.asarray(pp))   # ragged bank: B_e
 
     def widths(self, s, target):
         bd, cfg = self.bd, self.cfg
@@ -210,7 +215,7 @@ class Layer:
         s = i % N_XBATCH
         bank = self.banks[i % N_COPIES]
         shared = self.shared[i % N_COPIES] if self.shared else None
-        if self.policy == "threshold" and ev is None:
+        if self.policy == "threshold" and ev is None and kev is None:
             bd.layer(bank, shared, self.xs[s], self.wr, self.bias, cfg.k, cfg.b_lo, target, y=self.y,
                      idx=self.idx[s], gate=self.gate[s], bits=self.bits[s], workspace=self.lws)
             return
@@ -268,34 +273,39 @@ class Layer:
         return (time.perf_counter() - t0) / steps
 
     def timed_events(self, target, steps):
-        """Eager steps on the current stream: HIP events around each FFN call
-        and around its gate/up and down kernels (recorded by the library on
-        the call's stream)."""
+        """Eager steps on the current stream: first HIP events around each FFN
+        call, then, in steps of their own (the marks split the call), events
+        around its gate/up and down kernels, recorded by the library on the
+        call's stream."""
         torch = self.torch
 
-        def evs(n):
+        def evs(n, k):
             out = []
             for _ in range(n):
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
                 for x in e:
                     x.record()            # creates the HIP event behind each
                 out.append(e)
             return out
-        warm, run = evs(N_XBATCH), evs(steps)
+        warm, call, kern = evs(N_XBATCH, 2), evs(steps, 2), evs(steps, 4)
         torch.cuda.synchronize()
         for i in range(N_XBATCH):
-            self.step(i, target, warm[i][:2], warm[i][2:])
+            self.step(i, target, warm[i])
         torch.cuda.synchronize()
         for i in range(steps):
-            self.step(i, target, run[i][:2], run[i][2:])
+            self.step(i, target, call[i])
         torch.cuda.synchronize()
-        ffn_ms = [e[0].elapsed_time(e[1]) for e in run]
-        w13_ms = [e[2].elapsed_time(e[3]) for e in run]
-        w2_ms = [e[4].elapsed_time(e[5]) for e in run]
+        for i in range(steps):
+            self.step(i, target, None, kern[i])
+        torch.cuda.synchronize()
+        ffn_ms = [e[0].elapsed_time(e[1]) for e in call]
+        w13_ms = [e[0].elapsed_time(e[1]) for e in kern]
+        w2_ms = [e[2].elapsed_time(e[3]) for e in kern]
         kb = []
         for i in range(steps):
             s = i % N_XBATCH
-            kb.append(kernel_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg))
+            kb.append(kernel_bytes(self.idx[s].cpu().numpy(), self.bits[s].cpu().numpy(), self.cfg,
+                                   expert_widths=self.expert_widths))
         cfg = self.cfg
         flops = 6.0 * cfg.d * cfg.f * self.T * cfg.k  # routed SwiGLU FFN: gate, up, down
 
@@ -316,7 +326,7 @@ def kernel_roofline(ev, traffic=None):
     a2 = ev["w2_bytes"] / (ev["w2_ms"] * 1e-3) / 1e9
     ac = ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": a13, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a13 / HBM_PEAK_GBS,
-            "traffic": traffic, "kernel": "k_ffn_ks gate/up + SwiGLU (moe_anyprec_ffn's dominant kernel)",
+            "traffic": traffic, "kernel": "gate/up + SwiGLU streaming kernel (k_ffn<W13>; k_ffn_small<W13> for batches of a few tokens), the FFN stage's dominant kernel",
             "bytes_per_launch": ev["w13_bytes"], "us_per_launch": ev["w13_ms"] * 1e3,
             "down_kernel": {"achieved": a2, "frac": a2 / HBM_PEAK_GBS, "bytes_per_launch": ev["w2_bytes"],
                             "us_per_launch": ev["w2_ms"] * 1e3},
@@ -340,7 +350,8 @@ def cpu_baseline(cfg, w, budget_s=10.0):
         with threadpool_limits(limits=limit):
             tok = 0
             while time.perf_counter() - t0 < budget_s and tok < cfg.T:
-                rc = orc.bank_cache(w.routed)          # dequantisation is part of the work
+                rc = (orc.ragged_bank_cache(w.routed) if hasattr(w.routed, "plane_prefix")
+                      else orc.bank_cache(w.routed))   # dequantisation is part of the work
                 sc = orc.bank_cache(w.shared) if w.shared is not None else None
                 orc.layer(w.x_bf16, w.w_router, w.logit_bias, cfg.k, cfg.b_lo, cfg.b_max, cfg.target, rc, sc,
                           cfg.n_shared, tokens=[tok])
@@ -375,6 +386,8 @@ def main():
                     help="DuoRate per-expert widths solved on a prefill profile, then decode steps at those widths")
     ap.add_argument("--dpa", action="store_true",
                     help="DPA-MoE residual-aware chunk allocation over widths 1-4 on every decode step")
+    ap.add_argument("--ragged", action="store_true",
+                    help="the decode headline on a ragged bank: per-expert maximum widths B_e in {2, 3, 4}")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--target", type=float, default=3.0)
@@ -418,10 +431,10 @@ def main():
         return deepseek(args, torch, bd, wl)
     if args.duorate or args.dpa:
         return per_expert_modes(args, torch, bd, wl)
-    cfg = wl.config(2, T=args.tokens, target=args.target)
-    log("generating the Qwen3-30B-A3B-shaped layer (seeded)")
+    cfg = wl.config(2, T=args.tokens, target=args.target, ragged=args.ragged)
+    log("generating the Qwen3-30B-A3B-shaped layer (seeded)" + (", ragged bank" if args.ragged else ""))
     t0 = time.perf_counter()
-    w = wl.make_workload(cfg, keep_codes=False)
+    w = wl.make_ragged_workload(cfg, keep_codes=False) if args.ragged else wl.make_workload(cfg, keep_codes=False)
     log(f"generated in {time.perf_counter() - t0:.1f} s; stored {w.routed.stored_bytes() / 1e6:.1f} MB per copy")
 
     layers = {}
@@ -481,11 +494,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer, decode", "tokens": T, "hidden": cfg.d,
+        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer, decode" +
+                               (", ragged bank (per-expert maximum width 2/3/4)" if args.ragged else ""),
+                   "tokens": T, "hidden": cfg.d,
                    "expert_intermediate": cfg.f, "experts": cfg.E, "top_k": cfg.k, "bitplanes": cfg.b_max,
                    "group": cfg.g, "b_lo": cfg.b_lo, "target_avg_bits": args.target,
                    "weight_copies_rotated": N_COPIES, "activation_batches": N_XBATCH},
         "step_gbs": step_bytes / t_step / 1e9,
+        "stored_bytes_per_copy": w.routed.stored_bytes(),
         "bits_read": ev["bits_read"],
         "bits_alloc": ev["bits_alloc"],
         "n_active_experts": ev["n_active"],

@@ -34,7 +34,7 @@ class ExpertBankC(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("b_max", ctypes.c_int32),
                 ("w13_planes", ctypes.c_void_p), ("w13_sz", ctypes.c_void_p),
-                ("w2_planes", ctypes.c_void_p), ("w2_sz", ctypes.c_void_p)]
+                ("w2_planes", ctypes.c_void_p), ("w2_sz", ctypes.c_void_p), ("plane_prefix", ctypes.c_void_p)]
 
 
 _lib = None
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "moe_residual_to_bf16": (i32, [vp, vp, i64, vp]),
             "moe_rmsnorm_to_bf16": (i32, [vp, vp, i32, i32, f32, vp]),
             "moe_bits_from_threshold": (i32, [vp, i32, f32, i32, i32, vp, vp]),
+            "moe_bits_from_threshold_device": (i32, [vp, i32, vp, i32, i32, vp, vp]),
             "moe_stream_read": (i32, [vp, i64, vp, vp]),
             "moe_duorate_bake": (i32, [bp, vp, vp]),
             "moe_duorate_profile": (i32, [vp, i32, i32, vp, i32, i32, vp, vp, vp]),
@@ -136,6 +137,7 @@ class DeviceBank:
     w13_sz: torch.Tensor
     w2_planes: torch.Tensor
     w2_sz: torch.Tensor
+    plane_prefix: Optional[torch.Tensor] = None   # ragged bank: int32 [E+1] (device)
 
     @classmethod
     def from_host(cls, bank, device="cuda") -> "DeviceBank":
@@ -144,19 +146,23 @@ class DeviceBank:
             if a.dtype == np.uint32:
                 a = a.view(np.int32)
             return torch.from_numpy(a).to(device)
+        pp = getattr(bank, "plane_prefix", None)
         return cls(bank.n_experts, bank.d, bank.f, bank.g, bank.b_max,
-                   up(bank.w13_planes), up(bank.w13_sz), up(bank.w2_planes), up(bank.w2_sz))
+                   up(bank.w13_planes), up(bank.w13_sz), up(bank.w2_planes), up(bank.w2_sz),
+                   None if pp is None else up(np.asarray(pp, dtype=np.int32)))
 
     def clone(self) -> "DeviceBank":
         return DeviceBank(self.n_experts, self.d, self.f, self.g, self.b_max, self.w13_planes.clone(),
-                          self.w13_sz.clone(), self.w2_planes.clone(), self.w2_sz.clone())
+                          self.w13_sz.clone(), self.w2_planes.clone(), self.w2_sz.clone(),
+                          None if self.plane_prefix is None else self.plane_prefix.clone())
 
     def struct(self) -> ExpertBankC:
         for t in (self.w13_planes, self.w13_sz, self.w2_planes, self.w2_sz):
             _ptr(t, name="bank")
+        pp = None if self.plane_prefix is None else _ptr(self.plane_prefix, torch.int32, "plane_prefix")
         return ExpertBankC(self.n_experts, self.d, self.f, self.g, self.b_max,
                            self.w13_planes.data_ptr(), self.w13_sz.data_ptr(),
-                           self.w2_planes.data_ptr(), self.w2_sz.data_ptr())
+                           self.w2_planes.data_ptr(), self.w2_sz.data_ptr(), pp)
 
     def plane_bytes_per_expert(self, bits: int) -> int:
         """Bytes of the first `bits` planes of W13 and W2 of one expert."""
@@ -230,6 +236,40 @@ def bits_from_threshold(gate: torch.Tensor, tau: float, b_lo: int, b_max: int,
                                        _ptr(bits, torch.uint8, "bits"), _stream(stream))
     _check(st, "moe_bits_from_threshold")
     return bits
+
+
+def bits_from_threshold_device(gate: torch.Tensor, tau: torch.Tensor, b_lo: int, b_max: int,
+                               bits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Widths from a gate threshold held on the device (float32 scalar tensor)."""
+    P = gate.numel()
+    if bits is None:
+        bits = torch.empty(P, dtype=torch.uint8, device=gate.device)
+    st = lib().moe_bits_from_threshold_device(_ptr(gate, torch.float32, "gate"), P, _ptr(tau, torch.float32, "tau"),
+                                              b_lo, b_max, _ptr(bits, torch.uint8, "bits"), _stream(stream))
+    _check(st, "moe_bits_from_threshold_device")
+    return bits
+
+
+class ThresholdController:
+    """Calibration-threshold mode under a changing target: tau lives on the
+    device and is re-bisected over the stored calibration gate scores
+    (moe_alloc_bits) whenever the target changes; every step's widths come
+    from it (moe_bits_from_threshold_device).  Only argument marshalling and
+    the change test are done here."""
+
+    def __init__(self, calib_gates: torch.Tensor, b_lo: int, b_max: int):
+        self.cal = calib_gates.reshape(-1).contiguous()
+        self.b_lo, self.b_max = b_lo, b_max
+        self.tau = torch.empty(1, dtype=torch.float32, device=self.cal.device)
+        self._scratch = torch.empty(self.cal.numel(), dtype=torch.uint8, device=self.cal.device)
+        self.target = None
+
+    def widths(self, gate: torch.Tensor, target: float, bits: Optional[torch.Tensor] = None, stream=None):
+        if target != self.target:
+            alloc_bits(self.cal, self.b_lo, self.b_max, target, bits=self._scratch, tau=self.tau, stream=stream)
+            self.target = target
+        return bits_from_threshold_device(gate.reshape(-1), self.tau, self.b_lo, self.b_max, bits=bits,
+                                          stream=stream)
 
 
 def ffn_workspace_bytes(routed: DeviceBank, shared: Optional[DeviceBank], T: int, top_k: int) -> int:

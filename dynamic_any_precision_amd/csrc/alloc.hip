@@ -95,7 +95,24 @@ __global__ __launch_bounds__(256) void k_bits_threshold(const float* __restrict_
   if (i < P) bits[i] = (uint8_t)(gate[i] > tau ? b_max : b_lo);
 }
 
+// The same with tau read from device memory (written there by the allocation
+// kernel's tau output, so a changed target needs no host round trip).
+__global__ __launch_bounds__(256) void k_bits_threshold_dev(const float* __restrict__ gate, int P,
+                                                            const float* __restrict__ tau, int b_lo, int b_max,
+                                                            uint8_t* __restrict__ bits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const float t = *tau;
+  if (i < P) bits[i] = (uint8_t)(gate[i] > t ? b_max : b_lo);
+}
+
 }  // namespace
+
+hipError_t launch_bits_threshold_dev(const float* gate, int P, const float* tau, int b_lo, int b_max, uint8_t* bits,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(k_bits_threshold_dev, dim3((P + 255) / 256), dim3(256), 0, stream, gate, P, tau, b_lo, b_max,
+                     bits);
+  return hipGetLastError();
+}
 
 hipError_t launch_bits_threshold(const float* gate, int P, float tau, int b_lo, int b_max, uint8_t* bits,
                                  hipStream_t stream) {

@@ -99,8 +99,10 @@ moe_status ffn_shape(const moe_expert_bank* routed, const moe_expert_bank* share
   }
   if (T < 0 || top_k < 1 || top_k > 8 || top_k > routed->n_experts || routed->n_experts > 256) return MOE_ERR_RANGE;
   if ((int64_t)T * top_k + (shared ? (int64_t)shared->n_experts * T : 0) >= (1 << 24)) return MOE_ERR_RANGE;
+  if (shared && shared->plane_prefix) return MOE_ERR_UNSUPPORTED;  // shared banks are uniform
   *out = moe::make_shape(T, top_k, routed->n_experts, routed->b_max, routed->group, routed->d_model, routed->d_ff,
                          shared ? shared->n_experts : 0, shared ? shared->d_ff : 0);
+  out->bprefix = routed->plane_prefix;
   return MOE_OK;
 }
 
@@ -142,7 +144,6 @@ int record_hip_error(hipError_t e) {
   return MOE_ERR_HIP;
 }
 }  // namespace moe
-
 
 extern "C" {
 
@@ -208,6 +209,14 @@ moe_status moe_bits_from_threshold(const float* gate, int32_t P, float tau, int3
   if (P == 0) return MOE_OK;
   if (!gate || !bits) return MOE_ERR_NULL;
   return hip_status(moe::launch_bits_threshold(gate, P, tau, b_lo, b_max, bits, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_bits_from_threshold_device(const float* gate, int32_t P, const float* tau, int32_t b_lo,
+                                          int32_t b_max, uint8_t* bits, void* stream) {
+  if (P < 0 || b_lo < 1 || b_max > 4 || b_lo > b_max) return MOE_ERR_RANGE;
+  if (P == 0) return MOE_OK;
+  if (!gate || !tau || !bits) return MOE_ERR_NULL;
+  return hip_status(moe::launch_bits_threshold_dev(gate, P, tau, b_lo, b_max, bits, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_ffn_workspace_bytes(const moe_expert_bank* routed, const moe_expert_bank* shared, int32_t T,
@@ -313,7 +322,7 @@ moe_status moe_dequant(const moe_expert_bank* bank, int32_t expert, int32_t matr
     return MOE_ERR_RANGE;
   if (!out) return MOE_ERR_NULL;
   const moe::MatrixDev m = matrix == 0 ? w13_of(bank) : w2_of(bank);
-  return hip_status(moe::launch_dequant(m, bank->b_max, bank->group, expert, bits, out,
+  return hip_status(moe::launch_dequant(m, bank->b_max, bank->group, expert, bits, bank->plane_prefix, out,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -334,6 +343,7 @@ moe_status moe_rmsnorm_to_bf16(const float* h, uint16_t* x, int32_t rows, int32_
 moe_status moe_duorate_bake(const moe_expert_bank* bank, double* delta, void* stream) {
   moe_status st = check_bank(bank, true);
   if (st != MOE_OK) return st;
+  if (bank->plane_prefix) return MOE_ERR_UNSUPPORTED;
   if (!delta) return MOE_ERR_NULL;
   if (!aligned(delta, 8)) return MOE_ERR_ALIGN;
   return hip_status(moe::launch_duo_bake(w13_of(bank), bank->b_max, bank->group, bank->n_experts, delta,
@@ -384,6 +394,7 @@ moe_status moe_dpa_residuals(const moe_expert_bank* bank, double* resid, void* w
                              void* stream) {
   moe_status st = check_bank(bank, true);
   if (st != MOE_OK) return st;
+  if (bank->plane_prefix) return MOE_ERR_UNSUPPORTED;
   if (!resid || !workspace) return MOE_ERR_NULL;
   if (!aligned(resid, 8) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
   if (ws_bytes < moe_dpa_residuals_workspace_bytes(bank)) return MOE_ERR_WORKSPACE;

@@ -12,7 +12,7 @@ namespace {
 // the bracket is exact in fp32 (a multiple of 1/2 below 16 in size).
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ planes, const float* __restrict__ sz,
                                                  int N, int K, int B, int g, int expert, int bits,
-                                                 float* __restrict__ out) {
+                                                 const int* __restrict__ bprefix, float* __restrict__ out) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)N * K) return;
   const int n = (int)(idx / K), c = (int)(idx % K);
@@ -20,7 +20,14 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ pl
   const int tile = n >> 4, r = n & 15;
   const int kb = c >> 7, j = (c >> 5) & 3, bit = c & 31;
   const size_t word = (size_t)tile * (K / 2) + 64 * kb + 16 * j + r;
-  const uint32_t* base = planes + (size_t)expert * B * plane_words;
+  // a ragged bank: the expert's own first plane and width, read at most that wide
+  size_t first = (size_t)expert * B;
+  if (bprefix) {
+    first = (size_t)bprefix[expert];
+    B = bprefix[expert + 1] - bprefix[expert];
+    bits = bits < B ? bits : B;
+  }
+  const uint32_t* base = planes + first * plane_words;
   uint32_t q = 0;
   for (int p = 0; p < bits; ++p) q = (q << 1) | ((base[p * plane_words + word] >> bit) & 1u);
   const int delta = B - bits;
@@ -95,11 +102,12 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream) {
+hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, const int* bprefix, float* out,
+                          hipStream_t stream) {
   const size_t total = (size_t)m.N * m.K;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(256), 0, stream, m.planes, m.sz, m.N, m.K, B, g, expert, bits,
-                     out);
+                     bprefix, out);
   return hipGetLastError();
 }
 

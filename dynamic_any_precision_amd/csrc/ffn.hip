@@ -55,6 +55,7 @@ FfnShape make_shape(int T, int k, int E, int B, int g, int d, int f, int n_share
   s.max_rchunks = (E < s.P ? E : s.P) + s.P / s.cs + 1;
   s.n_schunks = n_shared * ((T + s.cs - 1) / s.cs);
   s.fmax = s.fs > f ? s.fs : f;
+  s.bprefix = nullptr;
   return s;
 }
 
@@ -165,6 +166,7 @@ struct FfnArgs {
   float2* hsgg;          // wide chunks: gate/up output group sums [block][fmax/g][16]
   int sub;               // 16-token blocks per chunk
   float* obuf;           // down output [Pt][d]
+  const int* bprefix;    // routed bank: per-expert plane prefix (null: every expert stores B planes)
 };
 
 // Raw buffer loads (resource flags of gfx9: 32-bit data format, untyped).
@@ -308,9 +310,21 @@ struct NextVal {
   int e, s0, m, mask, cnt;
 };
 
+// First plane and plane count of expert e: uniform banks store B planes per
+// expert; a ragged routed bank stores prefix[e+1] - prefix[e] from prefix[e].
+__device__ __forceinline__ void expert_planes(const int* bprefix, int B, int e, int& first, int& count) {
+  if (bprefix) {
+    first = uniform(bprefix[e]);
+    count = uniform(bprefix[e + 1]) - first;
+  } else {
+    first = e * B;
+    count = B;
+  }
+}
+
 template <int MODE, int QPK, int MASK>
-__device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, int c, int e, int s0, int m,
-                                         int cnt, int item, const NextRec& nr, NextVal& nv) {
+__device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
+                                         int s0, int m, int cnt, int item, const NextRec& nr, NextVal& nv) {
   constexpr Units U = make_units(MASK);
   constexpr Classes CL = make_classes(MASK);
   constexpr int BM = mask_bmax(MASK);
@@ -321,7 +335,8 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // token row of the activation operand; weight row of D
   const int jg = lane >> 4;   // k-chunk of the operands; token quad of D
-  const int B = a.B;
+  int pfirst, B;              // the expert's first plane and stored width
+  expert_planes(bprefix, a.B, e, pfirst, B);
   const int K = M.K;
   const int NKB = K >> 7;
   const int NQG = K / a.g;
@@ -357,7 +372,7 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, i
   const UnpackConst kc = unpack_const();
 
   const __amdgpu_buffer_rsrc_t rp =
-      make_rsrc(M.planes + (size_t)e * B * (plane_bytes / 4), (uint32_t)B * plane_bytes);
+      make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)c * a.act_stride, (uint32_t)K * 32);
@@ -707,7 +722,7 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
     switch (cur.mask & 15) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_item<MODE, QPK, MK>(a, M, c, cur.e, cur.s0, cur.m, cur.cnt, item, nr, nv); \
+    run_item<MODE, QPK, MK>(a, M, sh ? nullptr : a.bprefix, c, cur.e, cur.s0, cur.m, cur.cnt, item, nr, nv); \
     break;
       MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
       MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
@@ -729,6 +744,397 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
 
 
 // ---------------------------------------------------------------------------
+// Small batches: k-blocks of an item split over the waves of a workgroup.
+//
+// When the work items of a call can not fill the chip's waves (a handful of
+// tokens: at T = 1 the gate/up step has 8 x 48 items for 2048 wave slots),
+// each wave of the whole-K kernel above streams its item's 16 k-blocks as one
+// dependent chain.  Here each item gets a workgroup and its k-blocks are cut
+// four ways; the partial sums meet in LDS.
+
+constexpr int KS_WAVES = 4;
+
+template <int MODE, int QPK, int MASK>
+__device__ __forceinline__ void stream_part(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
+                                            int m, int cnt, int item, int kb0, int kb1, f32x4_t (&res)[2]) {
+  constexpr Units U = make_units(MASK);
+  constexpr Classes CL = make_classes(MASK);
+  constexpr int BM = mask_bmax(MASK);
+  constexpr int NT = 2;
+  constexpr int NP = NT / 2;
+  constexpr int PF = (QPK == 2 || CL.n >= 4) ? 1 : (ffn_wpe(MODE, QPK) > 2 ? FFN_W2_PF : FFN_PF);
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int jg = lane >> 4;
+  int pfirst, B;              // the expert's first plane and stored width
+  expert_planes(bprefix, a.B, e, pfirst, B);
+  const int K = M.K;
+  const int NQG = K / a.g;
+  const uint32_t plane_bytes = (uint32_t)((size_t)M.N * K / 8);
+
+  int tile[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    tile[t] = (MODE == MODE_W13) ? (t < NP ? item * NP + t : (M.N >> 5) + item * NP + (t - NP)) : item * NT + t;
+
+  float FA = 0.f, ctA = 0.f;
+  {
+    const int bt = width_of(cnt, r16);
+#pragma unroll
+    for (int u = 0; u < U.n; ++u)
+      if (bt >= U.p[u] + U.np[u]) FA += ldexpf(1.0f, B - 2 - U.p[u]);
+    ctA = bt > 0 ? 0.5f * (ldexpf(1.0f, B - bt) - 1.0f) : 0.f;
+  }
+  float fac[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bt = width_of(cnt, 4 * jg + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fac[k][i] = (k < CL.n && bt >= CL.w[k]) ? 1.0f : 0.0f;
+  }
+  uint32_t ubias[4];
+#pragma unroll
+  for (int u = 0; u < U.n; ++u) ubias[u] = vconst(unit_bias(B - 2 - U.p[u]));
+  const UnpackConst kc = unpack_const();
+
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
+  const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)c * a.act_stride, (uint32_t)K * 32);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)c * a.asum_stride, (uint32_t)a.asum_stride * 8);
+
+  const uint32_t vo_act = r16 < m ? lane * 16 : OOB;
+  const uint32_t vo_pl = lane * 4;
+  const uint32_t vo_s = r16 * 4;
+  constexpr int SPB = 4 / QPK;
+  uint32_t vo_x;
+  if (MODE == MODE_W13) {
+    vo_x = r16 < m ? (uint32_t)((jg % QPK) * 16 + r16) * 8 : OOB;
+  } else {
+    const int pidx = (QPK == 1) ? 2 * jg : 4 * (jg & 1) + 2 * (jg >> 1);
+    vo_x = r16 < m ? (uint32_t)(r16 * (a.fmax >> 4) + pidx) * 8 : OOB;
+  }
+
+  struct Ops {
+    u32x4_t act[4];
+    uint32_t w[NT][BM];
+    float s[NT][QPK], z[NT][QPK];
+    u32x4_t xs;
+  };
+  uint32_t toff[NT], soff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    toff[t] = (uint32_t)tile[t] * (K / 2) * 4;
+    soff[t] = (uint32_t)tile[t] * NQG * 128;
+  }
+  // local step j streams k-block kb0 + j; past the range every offset is out of range
+  const int NJ = kb1 - kb0;
+  auto load = [&](int j, Ops& o) {
+    const uint32_t oob = (j < NJ) ? 0u : OOB_STEP;
+    const int kb = kb0 + j;
+    const uint32_t va = vo_act + oob, vp = vo_pl + oob, vs = vo_s + oob, vx = vo_x + oob;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.act[i] = bld128(ra, va + i * 1024, kb * 4096);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int p = 0; p < BM; ++p) o.w[t][p] = bld32(rp, vp, toff[t] + kb * 256 + p * plane_bytes);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) {
+        o.s[t][h] = bldf(rs, vs, soff[t] + (kb * QPK + h) * 128);
+        o.z[t][h] = bldf(rs, vs, soff[t] + (kb * QPK + h) * 128 + 64);
+      }
+    if (MODE == MODE_W13) {
+      const float2 v = bld64f(rx, (jg / QPK == kb % SPB) ? vx : OOB, kb * QPK * 128);
+      o.xs = u32x4_t{__float_as_uint(v.x), __float_as_uint(v.y), 0u, 0u};
+    } else {
+      o.xs = bld128(rx, vx, kb * 64);
+    }
+  };
+
+  f32x4_t out[NT], corr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) out[t] = corr[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float cAk = 0.f, cAx = 0.f, cBs[NT], cBz[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) cBs[t] = cBz[t] = 0.f;
+  const uint32_t hmask0 = (QPK == 2 && (jg >> 1) != 0) ? 0u : 0xFFFFFFFFu;
+  const uint32_t hmask1 = (QPK == 2 && (jg >> 1) != 1) ? 0u : 0xFFFFFFFFu;
+
+  auto tile_mfma = [&](const u32x4_t (&act)[QPK][4], const uint32_t (&w)[BM], f32x4_t (&acc)[4][QPK]) {
+#pragma unroll
+    for (int k = 0; k < CL.n; ++k)
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) acc[k][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U.n; ++u) {
+      const uint32_t hi = w[U.p[u]];
+      const uint32_t lo = (U.np[u] == 2) ? w[U.p[u] + 1] : 0u;
+      u32x4_t W[4];
+      unpack_unit(hi, lo, U.np[u] == 2, ubias[u], kc, W);
+      const int k = CL.of_unit[u];
+#pragma unroll
+      for (int h = 0; h < QPK; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[k][h] = mfma_bf16(as_bf16x8(act[h][i]), as_bf16x8(W[i]), acc[k][h]);
+    }
+  };
+  auto tile_scale = [&](const f32x4_t (&acc)[4][QPK], const float (&s)[QPK], f32x4_t& o) {
+#pragma unroll
+    for (int h = 0; h < QPK; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[0][h][i];
+#pragma unroll
+        for (int k = 1; k < CL.n; ++k) v += fac[k][i] * acc[k][h][i];
+        o[i] += s[h] * v;
+      }
+    }
+  };
+  auto tile_corr = [&](float Kc, float X, const float (&s)[QPK], const float (&z)[QPK], f32x4_t& cr) {
+    const float sb = (QPK == 2 && (jg & 1)) ? s[QPK - 1] : s[0];
+    const float zb = (QPK == 2 && (jg & 1)) ? z[QPK - 1] : z[0];
+    cr = mfma_f32(Kc, sb, cr);
+    cr = mfma_f32(X, -sb * zb, cr);
+  };
+
+  constexpr bool STAGGER = CL.n < 3;
+  f32x4_t accb[2][4][QPK];
+  float sprev[QPK];
+#pragma unroll
+  for (int h = 0; h < QPK; ++h) {
+    sprev[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) accb[1][k][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](const Ops& o, int j) {
+    const int kb = kb0 + j;
+    u32x4_t act[QPK][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (QPK == 1) {
+        act[0][i] = o.act[i];
+      } else {
+        act[0][i] = o.act[i] & hmask0;
+        act[QPK - 1][i] = o.act[i] & hmask1;
+      }
+    }
+    float X, V;
+    if (MODE == MODE_W13) {
+      X = __uint_as_float(o.xs[0]);
+      V = __uint_as_float(o.xs[1]);
+    } else {
+      X = __uint_as_float(o.xs[0]) + __uint_as_float(o.xs[2]);
+      V = __uint_as_float(o.xs[1]) + __uint_as_float(o.xs[3]);
+    }
+    const float Kc = ctA * X - 128.0f * FA * V;
+    if (MODE == MODE_W13) {
+      const bool sel = (jg / QPK) == (kb % SPB);
+      const int h = jg % QPK;
+      cAk += Kc;
+      cAx += X;
+      if (sel) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          cBs[t] = o.s[t][QPK == 2 ? h : 0];
+          cBz[t] = -cBs[t] * o.z[t][QPK == 2 ? h : 0];
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (STAGGER) {
+        tile_mfma(act, o.w[t], accb[t & 1]);
+        if (t == 0) {
+          tile_scale(accb[1], sprev, out[NT - 1]);
+        } else {
+          tile_scale(accb[(t - 1) & 1], o.s[t - 1], out[t - 1]);
+        }
+      } else {
+        tile_mfma(act, o.w[t], accb[0]);
+        tile_scale(accb[0], o.s[t], out[t]);
+      }
+    }
+    if (STAGGER) {
+#pragma unroll
+      for (int h = 0; h < QPK; ++h) sprev[h] = o.s[NT - 1][h];
+    }
+    if (MODE == MODE_W13) {
+      if (kb % SPB == SPB - 1 || j == NJ - 1) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          corr[t] = mfma_f32(cAk, cBs[t], corr[t]);
+          corr[t] = mfma_f32(cAx, cBz[t], corr[t]);
+        }
+        cAk = cAx = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tile_corr(Kc, X, o.s[t], o.z[t], corr[t]);
+    }
+  };
+
+  Ops o[PF + 1];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    load(q, o[q]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int j0 = 0;
+  for (; j0 + PF + 1 <= NJ; j0 += PF + 1) {
+#pragma unroll
+    for (int q = 0; q <= PF; ++q) {
+      load(j0 + q + PF, o[(q + PF) % (PF + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(o[q], j0 + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+    if (j0 + q < NJ) compute(o[q], j0 + q);
+  if (STAGGER) tile_scale(accb[1], sprev, out[NT - 1]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) res[t] = out[t] + corr[t];
+}
+
+
+// Finish an item from its full sum (out + corr over every k-block): gate/up
+// -> SwiGLU, bf16 h in the down projection's fragment order and its 16-column
+// partial sums; down -> the per-slot output rows.
+template <int MODE>
+__device__ __forceinline__ void sk_finish(const FfnArgs& a, const f32x4_t (&res)[2], int c, int item, int s0, int m) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, jg = lane >> 4;
+  if (MODE == MODE_W13) {
+    const int u = item;  // row block of 16 h columns
+    const int n = u * 16 + r16;
+    const int cc = n & 31;
+    const int fp = frag_pos(cc);
+    const float ainv = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+    uint16_t* hrow = a.hg + (size_t)c * a.fmax * 16 +
+                     ((size_t)((n >> 7) * 4 + (fp >> 3)) * 64 + ((n & 127) >> 5) * 16) * 8 + (fp & 7);
+    float Xp[4], Vp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gval = res[0][i];
+      const float hval = gval / (1.0f + expf(-gval)) * res[1][i];
+      const float hf = bf16_to_f32(f32_to_bf16(hval));
+      if (4 * jg + i < m) hrow[(4 * jg + i) * 8] = (uint16_t)f32_to_bf16(hf * ainv);
+      Xp[i] = hf;
+      Vp[i] = hf * ainv;
+    }
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Xp[i] += __shfl_xor(Xp[i], msk, WAVE);
+        Vp[i] += __shfl_xor(Vp[i], msk, WAVE);
+      }
+    if (r16 == 0) {
+      float2* hs = a.hsg + (size_t)c * a.fmax + u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * jg + i < m) hs[(size_t)(4 * jg + i) * (a.fmax >> 4)] = make_float2(Xp[i], Vp[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 4 * jg + i;
+      if (tk < m) {
+        float* orow = a.obuf + (size_t)(s0 + tk) * a.d;
+        orow[(item * 2) * 16 + r16] = res[0][i];
+        orow[(item * 2 + 1) * 16 + r16] = res[1][i];
+      }
+    }
+  }
+}
+
+// An item's place: chunk, item within it, bank, and its chunk record.
+struct SkItem {
+  int c, item, sh, e, s0, m, mask, cnt, nkb;
+};
+
+__device__ __forceinline__ SkItem sk_item(const FfnArgs& a, int it) {
+  SkItem r;
+  const int items_r = a.meta[0] * a.items[0];
+  if (it < items_r) {
+    r.c = it / a.items[0];
+    r.item = it - r.c * a.items[0];
+    r.sh = 0;
+  } else {
+    const int w2 = it - items_r;
+    const int cs = w2 / a.items[1];
+    r.item = w2 - cs * a.items[1];
+    r.c = a.max_rchunks + cs;
+    r.sh = 1;
+  }
+  r.c = uniform(r.c);
+  r.item = uniform(r.item);
+  r.sh = uniform(r.sh);
+  const int4 ch = a.chunks[r.c];
+  r.e = uniform(ch.x);
+  r.s0 = uniform(ch.y);
+  r.m = uniform(ch.z);
+  r.mask = uniform(ch.w) & 15;
+  r.cnt = uniform(a.chunk_cnt[r.c]);
+  r.nkb = (r.sh ? a.m[1].K : a.m[0].K) >> 7;
+  return r;
+}
+
+template <int MODE, int QPK>
+__device__ __forceinline__ void sk_stream(const FfnArgs& a, const SkItem& it, int kb0, int kb1, f32x4_t (&res)[2]) {
+  const MatrixDev M = it.sh ? a.m[1] : a.m[0];
+  switch (it.mask) {
+#define MOE_CASE(MK) \
+  case MK:           \
+    stream_part<MODE, QPK, MK>(a, M, it.sh ? nullptr : a.bprefix, it.c, it.e, it.m, it.cnt, it.item, kb0, kb1, res); \
+    break;
+    MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+    MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
+#undef MOE_CASE
+    default:
+      res[0] = res[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      break;
+  }
+}
+
+// One item per workgroup, its k-blocks split over the four waves (wave q
+// streams k-blocks [q K/4, (q+1) K/4) of the item); wave 0 adds the four
+// partial sums from LDS in wave order and finishes the item.  Workgroup b
+// takes item b (an XCD-aware order keeps a chunk's items on one XCD); the
+// items past the call's routed chunks leave at once.
+template <int MODE, int QPK>
+__global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn_wpe(MODE, QPK), ffn_wpe(MODE, QPK)))) void k_ffn_small(FfnArgs a) {
+  __shared__ f32x4_t part[KS_WAVES][2][64];
+  const int wave = uniform((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int nwg = gridDim.x;
+  const int it = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int items = a.meta[0] * a.items[0] + a.n_schunks * a.items[1];
+  if (it >= items) return;  // the whole workgroup leaves together
+  const SkItem x = sk_item(a, it);
+  const int kb0 = uniform(wave * x.nkb / KS_WAVES), kb1 = uniform((wave + 1) * x.nkb / KS_WAVES);
+  f32x4_t res[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  if (kb0 < kb1) sk_stream<MODE, QPK>(a, x, kb0, kb1, res);
+  part[wave][0][lane] = res[0];
+  part[wave][1][lane] = res[1];
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t acc[2] = {part[0][0][lane], part[0][1][lane]};
+#pragma unroll
+    for (int q = 1; q < KS_WAVES; ++q) {
+      acc[0] += part[q][0][lane];
+      acc[1] += part[q][1][lane];
+    }
+    sk_finish<MODE>(a, acc, x.c, x.item, x.s0, x.m);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Wide chunks (prefill-sized batches): one workgroup of 4 waves per item, an
 // item being a chunk of <= 64 pairs (four 16-token blocks) and 4 row blocks
 // (gate/up: the gate and up tile of row blocks 4i..4i+3, one per wave; down:
@@ -741,8 +1147,8 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
 constexpr int WIDE_THREADS = 256;
 
 template <int MODE, int QPK, int MASK>
-__device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, int c, int e, int s0, int m, int item,
-                                         uint4* lds) {
+__device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
+                                         int s0, int m, int item, uint4* lds) {
   constexpr Units U = make_units(MASK);
   constexpr Classes CL = make_classes(MASK);
   constexpr int BM = mask_bmax(MASK);
@@ -750,7 +1156,8 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, i
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15, jg = lane >> 4;
-  const int B = a.B;
+  int pfirst, B;              // the expert's first plane and stored width
+  expert_planes(bprefix, a.B, e, pfirst, B);
   const int K = M.K;
   const int NKB = K >> 7;
   const int NQG = K / a.g;
@@ -787,7 +1194,7 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, i
   const UnpackConst kc = unpack_const();
 
   const __amdgpu_buffer_rsrc_t rp =
-      make_rsrc(M.planes + (size_t)e * B * (plane_bytes / 4), (uint32_t)B * plane_bytes);
+      make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
   const int nbk = (int)(a.act_stride / 2048);  // k-blocks per token block in the activation buffer
@@ -1022,7 +1429,7 @@ __global__ __launch_bounds__(WIDE_THREADS) __attribute__((amdgpu_waves_per_eu(2,
   switch (ch.w & 15) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_wide<MODE, QPK, MK>(a, M, c, ch.x, ch.y, ch.z, item, lds); \
+    run_wide<MODE, QPK, MK>(a, M, sh ? nullptr : a.bprefix, c, ch.x, ch.y, ch.z, item, lds); \
     break;
     MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
     MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
@@ -1104,6 +1511,7 @@ FfnArgs make_args(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev rou
   a.obuf = reinterpret_cast<float*>(ws + L.obuf);
   a.hsgg = reinterpret_cast<float2*>(ws + L.hsgg);
   a.sub = s.sub;
+  a.bprefix = s.bprefix;
   return a;
 }
 
@@ -1155,6 +1563,23 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
     return hipGetLastError();
   }
   const long max_items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
+  if (max_items <= (long)num_cu * ffn_wpe(mode, qpk) * 2) {
+    // at most one item per two wave slots: one workgroup per item, its
+    // k-blocks split over the workgroup's four waves
+    const int nwg = (int)((max_items + 7) & ~7L);
+    if (mode == MODE_W13) {
+      if (qpk == 2)
+        hipLaunchKernelGGL((k_ffn_small<MODE_W13, 2>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_ffn_small<MODE_W13, 1>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+    } else {
+      if (qpk == 2)
+        hipLaunchKernelGGL((k_ffn_small<MODE_W2, 2>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_ffn_small<MODE_W2, 1>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   long grid = (max_items + 3) / 4;
   // waves per SIMD x 4 SIMDs / 4 waves per block
   const long cap = (long)num_cu * ffn_wpe(mode, qpk);

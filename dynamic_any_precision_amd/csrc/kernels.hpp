@@ -24,6 +24,8 @@ hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_ma
                         int* n_hi_out, hipStream_t stream);
 hipError_t launch_bits_threshold(const float* gate, int P, float tau, int b_lo, int b_max, uint8_t* bits,
                                  hipStream_t stream);
+hipError_t launch_bits_threshold_dev(const float* gate, int P, const float* tau, int b_lo, int b_max, uint8_t* bits,
+                                     hipStream_t stream);
 
 // ---- FFN workspace plan
 struct FfnShape {
@@ -37,6 +39,7 @@ struct FfnShape {
   int fmax;              // max(f, fs)
   int cs;                // pairs per chunk: 16 (decode), or 64 (prefill: four 16-token blocks)
   int sub;               // 16-token blocks per chunk (cs / 16)
+  const int* bprefix;    // routed bank's per-expert plane prefix [E+1] (device), or null (uniform)
 };
 
 struct FfnLayout {
@@ -92,7 +95,8 @@ hipError_t launch_dpa_alloc(const float* gate, const int* idx, int P, const doub
                             hipStream_t stream);
 
 // ---- helpers
-hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, float* out, hipStream_t stream);
+hipError_t launch_dequant(MatrixDev m, int B, int g, int expert, int bits, const int* bprefix, float* out,
+                          hipStream_t stream);
 hipError_t launch_residual_to_bf16(const float* h, uint16_t* x, int64_t n, hipStream_t stream);
 hipError_t launch_rmsnorm_to_bf16(const float* h, uint16_t* x, int rows, int d, float eps, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int sink_len, hipStream_t stream);

@@ -52,6 +52,14 @@ struct PlanPtrs {
   int* expert_maxbits;
 };
 
+// A pair of expert e at width b reads min(b, B_e) planes (B_e the expert's
+// stored width; B for a uniform bank).
+__device__ __forceinline__ int clamp_width(const FfnShape& s, int e, int b) {
+  if (!s.bprefix) return b;
+  const int be = s.bprefix[e + 1] - s.bprefix[e];
+  return b < be ? b : be;
+}
+
 // Key e*B + (B - b) of pair i, or -1 for a dropped pair (err: bit 0 invalid
 // expert or width, bit 1 repeated expert).
 __device__ int pair_key(const FfnShape& s, const int* __restrict__ idx, const uint8_t* __restrict__ bits, int i,
@@ -68,7 +76,7 @@ __device__ int pair_key(const FfnShape& s, const int* __restrict__ idx, const ui
       return -1;
     }
   }
-  return e * s.B + (s.B - b);
+  return e * s.B + (s.B - clamp_width(s, e, b));
 }
 
 // Flat exclusive scan of the popcounts of n LDS words (block of PM_NT
@@ -191,7 +199,7 @@ __device__ void plan_small_core(const FfnShape& s, const PlanPtrs& pp, PlanSmall
         if (dup) {
           err |= 2;
         } else {
-          keys[r] = e * s.B + (s.B - L.sbits[i]);
+          keys[r] = e * s.B + (s.B - clamp_width(s, e, L.sbits[i]));
           const int t = i / s.k;
           atomicOr(&L.bm[keys[r] * W + (t >> 5)], 1u << (t & 31));
         }

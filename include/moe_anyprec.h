@@ -94,6 +94,19 @@ typedef enum {
  *
  *   Requirements: 1 <= n_experts; d_model, d_ff multiples of 128; group in
  *   {64, 128}; 1 <= b_max <= 4; planes and sz 16-byte aligned.
+ *
+ *   Per-expert maximum width (MatMoE review, Core Contribution: each expert's
+ *   maximum bit-width, 2/3/4, is chosen offline under a memory budget):
+ *   plane_prefix is NULL for a uniform bank (every expert stores b_max
+ *   planes), or a DEVICE int32 array [n_experts + 1] with plane_prefix[0] = 0
+ *   for a ragged bank: expert e stores B_e = plane_prefix[e+1] -
+ *   plane_prefix[e] planes (1 <= B_e <= b_max, b_max the largest), its codes
+ *   are B_e-bit, and its planes are planes plane_prefix[e] ..
+ *   plane_prefix[e+1]-1 of *_planes, viewed as [sum B_e][N/16 * 16*K/32]
+ *   (the same tiled words per plane; (scale, zero) keep their [E] layout).
+ *   A pair of width b reads min(b, B_e) planes, with floor and compensation
+ *   relative to B_e.  Only routed banks may be ragged; the DuoRate and DPA
+ *   bakes take uniform banks.  The prefix is not validated (a contract).
  */
 typedef struct {
   int32_t n_experts;
@@ -105,6 +118,7 @@ typedef struct {
   const float* w13_sz;
   const uint32_t* w2_planes;
   const float* w2_sz;
+  const int32_t* plane_prefix;
 } moe_expert_bank;
 
 /* ------------------------------------------------------------------------ */
@@ -179,6 +193,18 @@ moe_status moe_alloc_bits(const float* gate, int32_t P, int32_t b_lo, int32_t b_
  */
 moe_status moe_bits_from_threshold(const float* gate, int32_t P, float tau, int32_t b_lo, int32_t b_max,
                                    uint8_t* bits, void* stream);
+
+/*
+ * The same widths with tau read from device memory (a float32 scalar), for a
+ * controller that follows a changing target without a host round trip:
+ * when the target changes, moe_alloc_bits over the stored calibration gate
+ * scores writes the new tau to that scalar (its tau_out); every step then
+ * calls this with the routed gates.  NaN tau is a contract violation (every
+ * pair low).
+ * Ranges: P >= 0, 1 <= b_lo <= b_max <= 4.
+ */
+moe_status moe_bits_from_threshold_device(const float* gate, int32_t P, const float* tau, int32_t b_lo,
+                                          int32_t b_max, uint8_t* bits, void* stream);
 
 /* n* computed on the host exactly as moe_alloc_bits does (pure). */
 int32_t moe_budget_pairs(int32_t P, int32_t b_lo, int32_t b_max, float target_avg_bits);

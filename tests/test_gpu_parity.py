@@ -263,6 +263,36 @@ def test_calibrated_threshold_and_fixed_widths(kind):
         assert np.array_equal(bits.cpu().numpy().astype(np.int64), ref)
 
 
+def test_threshold_controller_follows_a_changing_target():
+    # a target that changes from step to step (a latency budget following the
+    # system load): tau is re-bisected on the device over the stored
+    # calibration gates when the target changes, and every step's widths
+    # equal the oracle's fixed-threshold widths for that target
+    w, dev, _, _ = workload(2)
+    cfg = w.cfg
+    wr = dev["w_router"]
+    cal = torch.cat([bd.route(bd.bf16_tensor(wl.step_activations(cfg, 700 + s, 32)), wr, None, cfg.k)[1].reshape(-1)
+                     for s in range(16)])
+    cal_np = cal.cpu().numpy().astype(np.float64)
+    ctl = bd.ThresholdController(cal, 2, 4)
+    targets = [3.0, 3.0, 2.5, 2.5, 2.5, 3.5, 2.0, 4.0, 3.25, 3.25, 2.75, 3.0]
+    avgs = []
+    for step, target in enumerate(targets):
+        x = bd.bf16_tensor(wl.step_activations(cfg, 800 + step, 32))
+        _, gate = bd.route(x, wr, None, cfg.k)
+        note(f"controller step {step} target {target}")
+        bits = ctl.widths(gate, target)
+        torch.cuda.synchronize()
+        tau_ref = orc.calibrate_threshold(cal_np, 2, 4, target)
+        assert float(ctl.tau.item()) == tau_ref, (step, target)
+        ref = orc.bits_from_threshold(gate.cpu().numpy().astype(np.float64), tau_ref, 2, 4)
+        got = bits.cpu().numpy().astype(np.int64)
+        assert np.array_equal(got, ref), (step, target)
+        avgs.append(float(got.mean()))
+    print("[controller] per-step targets " + " ".join(f"{t:g}" for t in targets), flush=True)
+    print("[controller] per-step averages " + " ".join(f"{a:.3f}" for a in avgs), flush=True)
+
+
 def test_fixed_widths_at_the_threshold_value():
     # scores equal to tau stay low; -inf makes every pair high; empty input
     g = torch.tensor([0.25, 0.5, 0.5, 0.75, 0.0, 1.0], dtype=torch.float32, device="cuda")
