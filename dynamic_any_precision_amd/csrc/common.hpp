@@ -62,6 +62,10 @@ __device__ __forceinline__ double wave_max_d(double v) {
   return v;
 }
 
+// s_waitcnt immediate that waits until at most n vector memory loads are
+// outstanding (n <= 63) and leaves the other counters unconstrained.
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // ---------------------------------------------------------------------------
 // Bitplane unpack into bf16 MFMA operands.
 //
@@ -101,7 +105,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // (x & m) | c: one v_and_or_b32 with m and c in VGPRs.  Written in plain C so
 // that the compiler sees the instruction: its results feed matrix-core
 // operands, and the wait states between the two are the compiler's to insert.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
+__host__ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
 
 struct UnpackConst {
   uint32_t m0, m1, m2;  // field masks at offsets 0, 2, 4 in both halves
@@ -138,6 +142,66 @@ __device__ __forceinline__ void unpack_unit(uint32_t hi, uint32_t lo, bool two, 
   o[1] = u32x4_t{and_or(E0, k.m2, bias), and_or(O0, k.m2, bias), and_or(E6, k.m0, bias), and_or(O6, k.m0, bias)};
   o[2] = u32x4_t{and_or(E6, k.m1, bias), and_or(O6, k.m1, bias), and_or(E6, k.m2, bias), and_or(O6, k.m2, bias)};
   o[3] = u32x4_t{and_or(E12, k.m0, bias), and_or(O12, k.m0, bias), and_or(E12, k.m1, bias), and_or(O12, k.m1, bias)};
+}
+
+// ---------------------------------------------------------------------------
+// Nibble expansion (wide chunks: one matrix-core pass per width).
+//
+// All planes of a lane's 32-column chunk of one row at once: plane p becomes
+// bit 3 - p of a 4-bit field per column, so the field of a pair read at
+// width b (planes p < b, the others zero) is f = ((q >> D) << D) * 2^(4 - B),
+// D = B - b.  Output word k (k = 0..15) carries column k in its low half and
+// column k + 16 in its high half, each as the bf16 value 2^e (128 + f 8^a)
+// with a = a_nib(k) and 2^e = 2^(B - 4) (the bias constant's exponent), so
+// a width-b operand is the full-width operand with the field bits of the
+// planes p >= b cleared (`nib_width_mask`).  Activations meeting word k are
+// pre-scaled by 8^-a; the products then sum to sum_c ((q >> D) << D)(c) x(c)
+// plus 2^(B - 4) 128 V, V the 8^-a-weighted sum, removed through the group
+// sums.  Two plane pairs are merged into 2-bit fields (columns 2j and 2j+1),
+// the two pairs into nibbles of columns 4j + r (one word per r), and each
+// output word is one shift and one AND-OR of those: 44 ALU operations per
+// chunk of 32 columns at any width.
+//
+// MFMA i takes words 4i..4i+3 as for `unpack_unit`, so all of MFMA i's words
+// share a = i & 1.
+
+__host__ __device__ constexpr int a_nib(int k) { return (k >> 2) & 1; }
+
+__host__ __device__ __forceinline__ uint32_t bit_insert(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// Field mask of width b (planes 0..b-1 kept) for the words of MFMA i, bias
+// bits included.
+__host__ __device__ constexpr uint32_t nib_width_mask(int b, int i) {
+  return 0xFF80FF80u | ((((0xFu << (4 - b)) & 0xFu) << (3 * (i & 1))) * 0x10001u);
+}
+
+struct NibConst {
+  uint32_t e2, e4, f0, f3;  // 2-bit lane masks, nibble lane masks, field masks at offsets 0 and 3
+};
+
+__host__ __device__ __forceinline__ NibConst nib_const_plain() {
+  return NibConst{0xAAAAAAAAu, 0xCCCCCCCCu, 0x000F000Fu, 0x00780078u};
+}
+
+// n3..n0: the plane words of nibble bits 3..0 (plane 0 is n3).
+__host__ __device__ __forceinline__ void unpack_nib(uint32_t n3, uint32_t n2, uint32_t n1, uint32_t n0, uint32_t bias,
+                                                    NibConst k, u32x4_t (&o)[4]) {
+  const uint32_t Eh = bit_insert(k.e2, n3 << 1, n2);  // columns 2j: (bit 3, bit 2) at bits 2j+1, 2j
+  const uint32_t Oh = bit_insert(k.e2, n3, n2 >> 1);  // columns 2j+1
+  const uint32_t El = bit_insert(k.e2, n1 << 1, n0);
+  const uint32_t Ol = bit_insert(k.e2, n1, n0 >> 1);
+  uint32_t Q[4];
+  Q[0] = bit_insert(k.e4, Eh << 2, El);  // nibble j = column 4j
+  Q[1] = bit_insert(k.e4, Oh << 2, Ol);  // column 4j + 1
+  Q[2] = bit_insert(k.e4, Eh, El >> 2);  // column 4j + 2
+  Q[3] = bit_insert(k.e4, Oh, Ol >> 2);  // column 4j + 3
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o[0][r] = and_or(Q[r], k.f0, bias);
+    o[1][r] = and_or(Q[r] >> 1, k.f3, bias);
+    o[2][r] = and_or(Q[r] >> 8, k.f0, bias);
+    o[3][r] = and_or(Q[r] >> 9, k.f3, bias);
+  }
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }

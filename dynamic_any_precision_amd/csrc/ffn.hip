@@ -202,9 +202,9 @@ __device__ __forceinline__ int width_of(int cnt, int t) {
 
 // ---------------------------------------------------------------------------
 // Activation gather: one block per (chunk, 128-column k-block).  Token rows
-// of the chunk are read (zero rows past its length), scaled by 4^-a, put in
-// fragment order through LDS and written as 4 KiB contiguous; the plain and
-// 4^-a-weighted sums of every quant group go beside them.
+// of the chunk are read (zero rows past its length), scaled by 4^-a (8^-a
+// for wide chunks), put in fragment order through LDS and written as 4 KiB
+// contiguous; the plain and scaled sums of every quant group go beside them.
 
 struct GatherArgs {
   const uint16_t* x;
@@ -242,7 +242,9 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
     const int col = 8 * q + j;  // column within the k-block
     const int cc = col & 31;
     const float xf = bf16_to_f32((j & 1) ? (in[j >> 1] >> 16) : (in[j >> 1] & 0xFFFFu));
-    const float sc = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+    // 4^-a for the plane-unit operands of 16-pair chunks, 8^-a for the
+    // nibble operands of 64-pair chunks
+    const float sc = a.sub > 1 ? 1.0f / (float)(1 << (3 * a_nib(cc & 15))) : 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
     X += xf;
     V += xf * sc;
     const int fp = frag_pos(cc);
@@ -1140,17 +1142,19 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
 // (gate/up: the gate and up tile of row blocks 4i..4i+3, one per wave; down:
 // tiles 8i..8i+7, two per wave).  Per 128-column k-block the activation
 // fragments of the four token blocks (16 KiB) are copied into LDS once by
-// DMA and read by all four waves; each wave expands its tiles' plane units
-// once and feeds them to the four token blocks.  Double-buffered: the copies
-// and weight loads of k-block kb+1 run while kb is computed.
+// DMA and read by all four waves.  Each wave expands its tiles' planes once
+// per k-block into nibble operands (all planes at once, see `unpack_nib`;
+// the chunk's narrower widths by one AND per word) and runs, per token
+// block, one matrix-core pass per width that block holds: pairs are sorted
+// by width, so most blocks hold one width and take one pass.  Double-
+// buffered: the copies and weight loads of k-block kb+1 run while kb is
+// computed.
 
 constexpr int WIDE_THREADS = 256;
 
 template <int MODE, int QPK, int MASK>
 __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
-                                         int s0, int m, int item, uint4* lds) {
-  constexpr Units U = make_units(MASK);
-  constexpr Classes CL = make_classes(MASK);
+                                         int s0, int m, int cnt, int item, uint4* lds, float2* xsl, uint32_t* plds) {
   constexpr int BM = mask_bmax(MASK);
   constexpr int NB = 4;  // token blocks
   const int lane = threadIdx.x & 63;
@@ -1165,62 +1169,67 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   const int tile0 = (MODE == MODE_W13) ? item * 4 + wave : item * 8 + 2 * wave;
   const int tile1 = (MODE == MODE_W13) ? (M.N >> 5) + item * 4 + wave : item * 8 + 2 * wave + 1;
 
-  // per token block: correction weights of the A-view token r16, coverage of
-  // the D-view tokens 4jg+i
+  // per token block: correction weights of the A-view token r16 (one pass of
+  // factor 2^(B-4) for a live pair), its width, and the widths the block
+  // holds (bit b-1).  c_b = pairs of width >= b; pairs are sorted widest
+  // first.
   float FA[NB], ctA[NB];
-  int cov[NB][4];  // bit k set when D-view token 4jg+i of block b reads class k
+  uint32_t wda = 0u;  // A-view token widths, nibble b
+  int pres = 0;       // 4 bits per block
+  const float f_unit = ldexpf(1.0f, B - 4);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int ta = 16 * b + r16;
-    const int bt = ta < m ? (a.slot_info[s0 + ta] >> 24) : 0;
-    FA[b] = 0.f;
-#pragma unroll
-    for (int u = 0; u < U.n; ++u)
-      if (bt >= U.p[u] + U.np[u]) FA[b] += ldexpf(1.0f, B - 2 - U.p[u]);
+    const int bt = width_of(cnt, 16 * b + r16);
+    FA[b] = bt > 0 ? f_unit : 0.f;
     ctA[b] = bt > 0 ? 0.5f * (ldexpf(1.0f, B - bt) - 1.0f) : 0.f;
+    wda |= (uint32_t)bt << (4 * b);
+    int pr = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int td = 16 * b + 4 * jg + i;
-      const int bd = td < m ? (a.slot_info[s0 + td] >> 24) : 0;
-      int bits = 0;
-#pragma unroll
-      for (int k = 0; k < CL.n; ++k) bits |= (bd >= CL.w[k]) ? (1 << k) : 0;
-      cov[b][i] = bits;
+    for (int w = 1; w <= 4; ++w) {
+      const int cw = (cnt >> (8 * (w - 1))) & 255;
+      const int cw1 = w < 4 ? (cnt >> (8 * w)) & 255 : 0;
+      const int lo = cw1 > 16 * b ? cw1 : 16 * b;
+      const int hi = cw < 16 * b + 16 ? cw : 16 * b + 16;
+      if (lo < hi) pr |= 1 << (w - 1);
     }
+    pres |= (pr & MASK) << (4 * b);
   }
-  uint32_t ubias[4];
-#pragma unroll
-  for (int u = 0; u < U.n; ++u) ubias[u] = vconst(unit_bias(B - 2 - U.p[u]));
-  const UnpackConst kc = unpack_const();
+  pres = uniform(pres);
+  const uint32_t ubias = vconst(unit_bias(B - 4));
+  NibConst nk = nib_const_plain();
+  nk.e2 = vconst(nk.e2);
+  nk.e4 = vconst(nk.e4);
+  nk.f0 = vconst(nk.f0);
+  nk.f3 = vconst(nk.f3);
 
-  const __amdgpu_buffer_rsrc_t rp =
-      make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
   const int nbk = (int)(a.act_stride / 2048);  // k-blocks per token block in the activation buffer
-  const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(a.asum + (size_t)c * NB * a.asum_stride, (uint32_t)(NB * a.asum_stride * 8));
   const uint16_t* actc = a.act + (size_t)c * NB * a.act_stride;
 
   constexpr int SPB = 4 / QPK;
-  const uint32_t vo_pl = lane * 4, vo_s = r16 * 4;
-  // group sums (X, V) of group kb*QPK + (jg % QPK), token r16, in the lanes
-  // of the k-block's slot; one load per token block
-  const uint32_t vo_x = (uint32_t)((jg % QPK) * 16 + r16) * 8;
+  const uint32_t vo_s = r16 * 4;
   const uint32_t t0off = (uint32_t)tile0 * (K / 2) * 4, t1off = (uint32_t)tile1 * (K / 2) * 4;
   const uint32_t s0off = (uint32_t)tile0 * NQG * 128, s1off = (uint32_t)tile1 * NQG * 128;
 
+  // plane words of the wave's two tiles at k-block kb -> LDS (one dword per
+  // lane, plane and tile); scales and zeros into registers
+  const uint32_t* pe = M.planes + (size_t)pfirst * (plane_bytes / 4);
+  auto copy_planes = [&](int kb, int st) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int p = 0; p < BM; ++p) {
+        const uint32_t* src = pe + ((t ? t1off : t0off) + kb * 256 + p * plane_bytes) / 4 + lane;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)(plds + ((st * 4 + wave) * 2 + t) * 256 + p * 64),
+                                         4, 0, 0);
+      }
+  };
   struct Wts {
-    uint32_t w[2][BM];
     float s[2][QPK], z[2][QPK];
-    float2 xs[NB];
   };
   auto load_w = [&](int kb, Wts& o) {
-#pragma unroll
-    for (int p = 0; p < BM; ++p) {
-      o.w[0][p] = bld32(rp, vo_pl, t0off + kb * 256 + p * plane_bytes);
-      o.w[1][p] = bld32(rp, vo_pl, t1off + kb * 256 + p * plane_bytes);
-    }
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
       o.s[0][h] = bldf(rs, vo_s, s0off + (kb * QPK + h) * 128);
@@ -1228,9 +1237,15 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
       o.s[1][h] = bldf(rs, vo_s, s1off + (kb * QPK + h) * 128);
       o.z[1][h] = bldf(rs, vo_s, s1off + (kb * QPK + h) * 128 + 64);
     }
-    const uint32_t vx = (jg / QPK == kb % SPB) ? vo_x : OOB;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) o.xs[b] = bld64f(rx, vx, (uint32_t)(b * a.asum_stride * 8 + kb * QPK * 128));
+  };
+  // group sums (X, V) of k-block kb's groups -> LDS: wave w copies those of
+  // token block w (16 QPK float2, one dword per lane)
+  auto copy_xs = [&](int kb, int buf) {
+    if (lane < 32 * QPK) {
+      const float* src = reinterpret_cast<const float*>(a.asum + (size_t)(c * NB + wave) * a.asum_stride + kb * QPK * 16) + lane;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(xsl + (buf * NB + wave) * 32),
+                                       4, 0, 0);
+    }
   };
   // activation fragments of k-block kb for the four token blocks -> LDS
   // buffer: wave w copies token block w, 4 x 1 KiB
@@ -1261,8 +1276,10 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     const bool sel = (jg / QPK) == (kb % SPB);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      cAk[b] += ctA[b] * o.xs[b].x - 128.0f * FA[b] * o.xs[b].y;
-      cAx[b] += o.xs[b].x;
+      const float2 xv = xsl[(buf * NB + b) * 32 + (jg % QPK) * 16 + r16];
+      const float X = sel ? xv.x : 0.f, V = sel ? xv.y : 0.f;
+      cAk[b] += ctA[b] * X - 128.0f * FA[b] * V;
+      cAx[b] += X;
     }
     if (sel) {
       const int h = jg % QPK;
@@ -1274,49 +1291,86 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      // operands of every width the chunk holds: the widest from the planes,
+      // the narrower ones by clearing field bits
       u32x4_t W[4][4];
-#pragma unroll
-      for (int u = 0; u < U.n; ++u) {
-        const uint32_t hi = o.w[t][U.p[u]];
-        const uint32_t lo = (U.np[u] == 2) ? o.w[t][U.p[u] + 1] : 0u;
-        unpack_unit(hi, lo, U.np[u] == 2, ubias[u], kc, W[u]);
+      {
+        const uint32_t* pw = plds + ((buf * 4 + wave) * 2 + t) * 256 + lane;
+        const uint32_t n3 = pw[0];
+        const uint32_t n2 = BM > 1 ? pw[64] : 0u;
+        const uint32_t n1 = BM > 2 ? pw[128] : 0u;
+        const uint32_t n0 = BM > 3 ? pw[192] : 0u;
+        unpack_nib(n3, n2, n1, n0, ubias, nk, W[BM - 1]);
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4* src = lds + (size_t)(buf * NB + b) * 256 + lane;
-        u32x4_t act[QPK][4];
+      for (int w = 1; w < BM; ++w)
+        if (MASK & (1 << (w - 1))) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t v = as_u32x4(src[i * 64]);
-          if (QPK == 1) {
-            act[0][i] = v;
-          } else {
-            act[0][i] = v & hmask0;
-            act[QPK - 1][i] = v & hmask1;
-          }
+          for (int i = 0; i < 4; ++i) W[w - 1][i] = W[BM - 1][i] & nib_width_mask(w, i);
         }
-        f32x4_t acc[4][QPK];
+      // Per token block one accumulator: a block of one width takes one
+      // pass; a block holding several widths takes one pass per width with
+      // the activation rows of the other widths cleared.  Each block is
+      // scaled after the next block's products are issued, so the scaling
+      // does not wait on the products just issued; the next block's
+      // activations are read from LDS while the current block's products run.
+      // One branch per token block (uniform): a block of one width w runs
+      // one pass on the width-w operand; a block holding several widths runs
+      // one pass per width with the activation rows of the other widths
+      // cleared.  Each branch scales its own products, so no accumulator is
+      // carried across branches.  The next block's activations are read from
+      // LDS (double-buffered by block parity) while the current block runs.
+      u32x4_t av[2][4];
 #pragma unroll
-        for (int k = 0; k < CL.n; ++k)
+      for (int i = 0; i < 4; ++i) av[0][i] = as_u32x4(lds[(size_t)(buf * NB) * 256 + lane + i * 64]);
 #pragma unroll
-          for (int h = 0; h < QPK; ++h) acc[k][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NB; ++b) {
+        const int cb = b & 1;
+        if (b + 1 < NB) {
 #pragma unroll
-        for (int u = 0; u < U.n; ++u) {
-          const int k = CL.of_unit[u];
+          for (int i = 0; i < 4; ++i) av[cb ^ 1][i] = as_u32x4(lds[(size_t)(buf * NB + b + 1) * 256 + lane + i * 64]);
+        }
+        const int pb = (pres >> (4 * b)) & 15;
+#pragma unroll
+        for (int w = 4; w >= 1; --w) {
+          if (!(MASK & (1 << (w - 1)))) continue;
+          if (pb != (1 << (w - 1))) continue;  // uniform: the block holds width w only
+          f32x4_t acc[QPK];
+#pragma unroll
+          for (int h = 0; h < QPK; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[0] = mfma_bf16(as_bf16x8(QPK == 1 ? av[cb][i] : (av[cb][i] & hmask0)), as_bf16x8(W[w - 1][i]), acc[0]);
+            if (QPK == 2) acc[QPK - 1] = mfma_bf16(as_bf16x8(av[cb][i] & hmask1), as_bf16x8(W[w - 1][i]), acc[QPK - 1]);
+          }
 #pragma unroll
           for (int h = 0; h < QPK; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[k][h] = mfma_bf16(as_bf16x8(act[h][i]), as_bf16x8(W[u][i]), acc[k][h]);
+            for (int i = 0; i < 4; ++i) out[t][b][i] += o.s[t][h] * acc[h][i];
         }
+        if (pb & (pb - 1)) {  // uniform: several widths
+          f32x4_t acc[QPK];
 #pragma unroll
-        for (int h = 0; h < QPK; ++h) {
+          for (int h = 0; h < QPK; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // the widths are re-read here so that their comparisons are not
+          // kept live across the stream
+          const uint32_t wa = (vconst(wda) >> (4 * b)) & 15u;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = acc[0][h][i];
+          for (int w = 4; w >= 1; --w) {
+            if (!(MASK & (1 << (w - 1)))) continue;
+            if (!(pb & (1 << (w - 1)))) continue;
+            const uint32_t am = wa == (uint32_t)w ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-            for (int k = 1; k < CL.n; ++k) v += ((cov[b][i] >> k) & 1) ? acc[k][h][i] : 0.f;
-            out[t][b][i] += o.s[t][h] * v;
+            for (int i = 0; i < 4; ++i) {
+              acc[0] = mfma_bf16(as_bf16x8(av[cb][i] & (am & hmask0)), as_bf16x8(W[w - 1][i]), acc[0]);
+              if (QPK == 2)
+                acc[QPK - 1] = mfma_bf16(as_bf16x8(av[cb][i] & (am & hmask1)), as_bf16x8(W[w - 1][i]), acc[QPK - 1]);
+            }
           }
+#pragma unroll
+          for (int h = 0; h < QPK; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[t][b][i] += o.s[t][h] * acc[h][i];
         }
       }
     }
@@ -1333,27 +1387,35 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     }
   };
 
-  Wts wa, wb;
-  copy_act(0, 0);
-  load_w(0, wa);
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero
-  __syncthreads();
-  for (int kb = 0; kb < NKB; kb += 2) {
-    if (kb + 1 < NKB) {
-      copy_act(kb + 1, 1);
-      load_w(kb + 1, wb);
-    }
-    compute(wa, kb, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kb + 1 < NKB) {
-      if (kb + 2 < NKB) {
-        copy_act(kb + 2, 0);
-        load_w(kb + 2, wa);
+  // Three-stage ring: k-block kb+2's copies and weight loads are issued
+  // once every wave has passed k-block kb's barrier (so its LDS buffer,
+  // last read at kb-1, is free) and run while kb and kb+1 are computed.
+  // Every stage issues the same NS vector loads and they retire in issue
+  // order, so waiting for all but the newest NS leaves exactly stage kb+1 in
+  // flight.
+  constexpr int NS = 4 + 1 + 2 * BM + 4 * QPK;  // activation and group-sum copies, plane copies, scales and zeros
+  Wts wr[3];
+  auto issue = [&](int kb, int st) {
+    copy_act(kb, st);
+    copy_xs(kb, st);
+    copy_planes(kb, st);
+    load_w(kb, wr[st]);
+  };
+  issue(0, 0);
+  if (NKB > 1) issue(1, 1);
+  for (int kb0 = 0; kb0 < NKB; kb0 += 3) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int kb = kb0 + q;
+      if (kb < NKB) {
+        if (kb + 1 < NKB)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NS));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (kb + 2 < NKB) issue(kb + 2, (q + 2) % 3);
+        compute(wr[q], kb, q);
       }
-      compute(wb, kb + 1, 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
     }
   }
 
@@ -1366,7 +1428,7 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
       const int n = u * 16 + r16;
       const int cc = n & 31;
       const int fp = frag_pos(cc);
-      const float ainv = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+      const float ainv = 1.0f / (float)(1 << (3 * a_nib(cc & 15)));
       uint16_t* hrow = a.hg + (size_t)bid * a.fmax * 16 +
                        ((size_t)((n >> 7) * 4 + (fp >> 3)) * 64 + ((n & 127) >> 5) * 16) * 8 + (fp & 7);
       float Xp[4], Vp[4];
@@ -1407,11 +1469,19 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
 
 template <int MODE, int QPK>
 __global__ __launch_bounds__(WIDE_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_wide(FfnArgs a) {
-  __shared__ uint4 lds[2 * 4 * 256];  // two k-blocks x four token blocks x 4 KiB
+  __shared__ uint4 lds[3 * 4 * 256];   // three k-blocks x four token blocks x 4 KiB
+  __shared__ float2 xsl[3 * 4 * 32];   // their group sums
+  __shared__ uint32_t plds[3 * 4 * 2 * 4 * 64];  // per k-block, wave, tile and plane: 64 plane words
+  // Workgroup b runs on XCD b mod 8 and takes item (b / 8) of that XCD's
+  // contiguous eighth of the call's items: the items of one chunk (which
+  // share its activations) and the chunks of one expert (which share its
+  // weights) then run at the same time on one XCD and meet in its L2.
   const int n_rc = a.meta[0];
   const int items_r = n_rc * a.items[0];
-  const int w = blockIdx.x;
-  if (w >= items_r + a.n_schunks * a.items[1]) return;
+  const int items = items_r + a.n_schunks * a.items[1];
+  const int xcd = blockIdx.x & 7;
+  const int w = (int)(((long)items * xcd) >> 3) + (int)(blockIdx.x >> 3);
+  if (w >= (int)(((long)items * (xcd + 1)) >> 3)) return;
   int c, item, sh;
   if (w < items_r) {
     c = w / a.items[0];
@@ -1425,11 +1495,12 @@ __global__ __launch_bounds__(WIDE_THREADS) __attribute__((amdgpu_waves_per_eu(2,
     sh = 1;
   }
   const int4 ch = a.chunks[c];
+  const int cnt = uniform(a.chunk_cnt[c]);
   const MatrixDev& M = a.m[sh];
   switch (ch.w & 15) {
 #define MOE_CASE(MK) \
   case MK:           \
-    run_wide<MODE, QPK, MK>(a, M, sh ? nullptr : a.bprefix, c, ch.x, ch.y, ch.z, item, lds); \
+    run_wide<MODE, QPK, MK>(a, M, sh ? nullptr : a.bprefix, c, ch.x, ch.y, ch.z, cnt, item, lds, xsl, plds); \
     break;
     MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
     MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15)
@@ -1548,17 +1619,19 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
       const int nb = (s.max_rchunks + s.n_schunks) * s.sub, ng = s.fmax / s.g;
       hipLaunchKernelGGL(k_hsum, dim3((nb * ng * 16 + 255) / 256), dim3(256), 0, stream, a, nb, ng);
     }
+    // 8 x ceil(items / 8) workgroups: every XCD's eighth of the items fits
     const long items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
+    const long grid = 8 * ((items + 7) / 8);
     if (mode == MODE_W13) {
       if (qpk == 2)
-        hipLaunchKernelGGL((k_wide<MODE_W13, 2>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_wide<MODE_W13, 2>), dim3(grid), dim3(WIDE_THREADS), 0, stream, a);
       else
-        hipLaunchKernelGGL((k_wide<MODE_W13, 1>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_wide<MODE_W13, 1>), dim3(grid), dim3(WIDE_THREADS), 0, stream, a);
     } else {
       if (qpk == 2)
-        hipLaunchKernelGGL((k_wide<MODE_W2, 2>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_wide<MODE_W2, 2>), dim3(grid), dim3(WIDE_THREADS), 0, stream, a);
       else
-        hipLaunchKernelGGL((k_wide<MODE_W2, 1>), dim3(items), dim3(WIDE_THREADS), 0, stream, a);
+        hipLaunchKernelGGL((k_wide<MODE_W2, 1>), dim3(grid), dim3(WIDE_THREADS), 0, stream, a);
     }
     return hipGetLastError();
   }
