@@ -1157,8 +1157,11 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
                                          int s0, int m, int cnt, int item, uint4* lds, float2* xsl, uint32_t* plds) {
   constexpr int BM = mask_bmax(MASK);
   constexpr int NB = 4;  // token blocks
+  // tiles whose operands are live at once: both when the chunk holds at most
+  // two widths (each block's activations then serve both), else one
+  constexpr int TP = (((MASK & 1) + ((MASK >> 1) & 1) + ((MASK >> 2) & 1) + ((MASK >> 3) & 1)) <= 2) ? 2 : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform((int)(threadIdx.x >> 6));  // wave-uniform: scalar resources and LDS bases
   const int r16 = lane & 15, jg = lane >> 4;
   int pfirst, B;              // the expert's first plane and stored width
   expert_planes(bprefix, a.B, e, pfirst, B);
@@ -1204,7 +1207,6 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
 
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
-  const int nbk = (int)(a.act_stride / 2048);  // k-blocks per token block in the activation buffer
   const uint16_t* actc = a.act + (size_t)c * NB * a.act_stride;
 
   constexpr int SPB = 4 / QPK;
@@ -1214,17 +1216,18 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
 
   // plane words of the wave's two tiles at k-block kb -> LDS (one dword per
   // lane, plane and tile); scales and zeros into registers
-  const uint32_t* pe = M.planes + (size_t)pfirst * (plane_bytes / 4);
+  // (buffer loads into LDS: a constant lane offset and a scalar step offset,
+  // so the per-step addressing is scalar work)
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rpl =
+      make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   auto copy_planes = [&](int kb, int st) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int p = 0; p < BM; ++p) {
-        const uint32_t* src = pe + ((t ? t1off : t0off) + kb * 256 + p * plane_bytes) / 4 + lane;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)(plds + ((st * 4 + wave) * 2 + t) * 256 + p * 64),
-                                         4, 0, 0);
-      }
+      for (int p = 0; p < BM; ++p)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rpl, (lds_ptr)(plds + ((st * 4 + wave) * 2 + t) * 256 + p * 64), 4,
+                                                 lane * 4, (t ? t1off : t0off) + kb * 256 + p * plane_bytes, 0, 0);
   };
   struct Wts {
     float s[2][QPK], z[2][QPK];
@@ -1240,24 +1243,21 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   };
   // group sums (X, V) of k-block kb's groups -> LDS: wave w copies those of
   // token block w (16 QPK float2, one dword per lane)
+  // (lanes past the 16 QPK float2 copy what follows them, never read)
+  const __amdgpu_buffer_rsrc_t rxs =
+      make_rsrc(a.asum + (size_t)(c * NB + wave) * a.asum_stride, (uint32_t)a.asum_stride * 8);
   auto copy_xs = [&](int kb, int buf) {
-    if (lane < 32 * QPK) {
-      const float* src = reinterpret_cast<const float*>(a.asum + (size_t)(c * NB + wave) * a.asum_stride + kb * QPK * 16) + lane;
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(xsl + (buf * NB + wave) * 32),
-                                       4, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr)(xsl + (buf * NB + wave) * 32), 4, lane * 4, kb * QPK * 128, 0, 0);
   };
   // activation fragments of k-block kb for the four token blocks -> LDS
   // buffer: wave w copies token block w, 4 x 1 KiB
+  const __amdgpu_buffer_rsrc_t ract = make_rsrc(actc + (size_t)wave * a.act_stride, (uint32_t)a.act_stride * 2);
   auto copy_act = [&](int kb, int buf) {
-    const uint16_t* src = actc + (size_t)wave * a.act_stride + (size_t)kb * 2048 + lane * 8;
     uint4* dst = lds + (size_t)(buf * NB + wave) * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src + i * 512), (__attribute__((address_space(3))) void*)(dst + i * 64),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ract, (lds_ptr)(dst + i * 64), 16, lane * 16, kb * 4096 + i * 1024, 0, 0);
   };
-  (void)nbk;
 
   f32x4_t out[2][NB];
 #pragma unroll
@@ -1272,6 +1272,10 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   const uint32_t hmask1 = (QPK == 2 && (jg >> 1) != 1) ? 0u : 0xFFFFFFFFu;
 
   auto compute = [&](const Wts& o, int kb, int buf) {
+    // the blocks' widths, re-read per k-block so that the branch conditions
+    // derived from them are not kept live (as lane masks) across the stream
+    int presk = pres;
+    asm volatile("" : "+s"(presk));
     // group terms of this k-block
     const bool sel = (jg / QPK) == (kb % SPB);
 #pragma unroll
@@ -1290,89 +1294,108 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // operands of every width the chunk holds: the widest from the planes,
-      // the narrower ones by clearing field bits
-      u32x4_t W[4][4];
-      {
-        const uint32_t* pw = plds + ((buf * 4 + wave) * 2 + t) * 256 + lane;
-        const uint32_t n3 = pw[0];
-        const uint32_t n2 = BM > 1 ? pw[64] : 0u;
-        const uint32_t n1 = BM > 2 ? pw[128] : 0u;
-        const uint32_t n0 = BM > 3 ? pw[192] : 0u;
-        unpack_nib(n3, n2, n1, n0, ubias, nk, W[BM - 1]);
+    for (int t0 = 0; t0 < 2; t0 += TP) {
+    // operands of every width the chunk holds, for the TP tiles of this
+    // pass: the widest from the planes, the narrower ones by clearing field
+    // bits
+    u32x4_t W[TP][4][4];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      const uint32_t* pw = plds + ((buf * 4 + wave) * 2 + t0 + t) * 256 + lane;
+      const uint32_t n3 = pw[0];
+      const uint32_t n2 = BM > 1 ? pw[64] : 0u;
+      const uint32_t n1 = BM > 2 ? pw[128] : 0u;
+      const uint32_t n0 = BM > 3 ? pw[192] : 0u;
+      unpack_nib(n3, n2, n1, n0, ubias, nk, W[t][BM - 1]);
+      if (MASK & ((1 << (BM - 1)) - 1)) {
+        // keep each widest word one AND-OR (re-associating it with the
+        // narrower widths' ANDs costs an extra operation per word)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) W[t][BM - 1][i][r] = vconst(W[t][BM - 1][i][r]);
       }
 #pragma unroll
       for (int w = 1; w < BM; ++w)
         if (MASK & (1 << (w - 1))) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) W[w - 1][i] = W[BM - 1][i] & nib_width_mask(w, i);
+          for (int i = 0; i < 4; ++i) W[t][w - 1][i] = W[t][BM - 1][i] & nib_width_mask(w, i);
         }
-      // Per token block one accumulator: a block of one width takes one
-      // pass; a block holding several widths takes one pass per width with
-      // the activation rows of the other widths cleared.  Each block is
-      // scaled after the next block's products are issued, so the scaling
-      // does not wait on the products just issued; the next block's
-      // activations are read from LDS while the current block's products run.
-      // One branch per token block (uniform): a block of one width w runs
-      // one pass on the width-w operand; a block holding several widths runs
-      // one pass per width with the activation rows of the other widths
-      // cleared.  Each branch scales its own products, so no accumulator is
-      // carried across branches.  The next block's activations are read from
-      // LDS (double-buffered by block parity) while the current block runs.
-      u32x4_t av[2][4];
+    }
+    // One uniform branch per token block: a block of one width w runs one
+    // pass per tile on the width-w operands; a block holding several widths
+    // runs one pass per width with the activation rows of the other widths
+    // cleared.  Each branch scales its own products (no accumulator is
+    // carried across branches); the tiles' chains are interleaved.  The
+    // block's activations are read from LDS once for the TP tiles, the next
+    // block's (double-buffered by block parity) while this one runs.
+    u32x4_t av[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[0][i] = as_u32x4(lds[(size_t)(buf * NB) * 256 + lane + i * 64]);
+    for (int i = 0; i < 4; ++i) av[0][i] = as_u32x4(lds[(size_t)(buf * NB) * 256 + lane + i * 64]);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int cb = b & 1;
-        if (b + 1 < NB) {
+    for (int b = 0; b < NB; ++b) {
+      const int cb = b & 1;
+      if (b + 1 < NB) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[cb ^ 1][i] = as_u32x4(lds[(size_t)(buf * NB + b + 1) * 256 + lane + i * 64]);
-        }
-        const int pb = (pres >> (4 * b)) & 15;
+        for (int i = 0; i < 4; ++i) av[cb ^ 1][i] = as_u32x4(lds[(size_t)(buf * NB + b + 1) * 256 + lane + i * 64]);
+      }
+      const int pb = (presk >> (4 * b)) & 15;
+#pragma unroll
+      for (int w = 4; w >= 1; --w) {
+        if (!(MASK & (1 << (w - 1)))) continue;
+        if (pb != (1 << (w - 1))) continue;  // uniform: the block holds width w only
+        f32x4_t acc[TP][QPK];
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
+#pragma unroll
+          for (int h = 0; h < QPK; ++h) acc[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            acc[t][0] = mfma_bf16(as_bf16x8(QPK == 1 ? av[cb][i] : (av[cb][i] & hmask0)), as_bf16x8(W[t][w - 1][i]), acc[t][0]);
+            if (QPK == 2) acc[t][QPK - 1] = mfma_bf16(as_bf16x8(av[cb][i] & hmask1), as_bf16x8(W[t][w - 1][i]), acc[t][QPK - 1]);
+          }
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
+#pragma unroll
+          for (int h = 0; h < QPK; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[t0 + t][b][i] += o.s[t0 + t][h] * acc[t][h][i];
+      }
+      if (pb & (pb - 1)) {  // uniform: several widths
+        f32x4_t acc[TP][QPK];
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
+#pragma unroll
+          for (int h = 0; h < QPK; ++h) acc[t][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // the widths are re-read here so that their comparisons are not
+        // kept live across the stream
+        const uint32_t wa = (vconst(wda) >> (4 * b)) & 15u;
 #pragma unroll
         for (int w = 4; w >= 1; --w) {
           if (!(MASK & (1 << (w - 1)))) continue;
-          if (pb != (1 << (w - 1))) continue;  // uniform: the block holds width w only
-          f32x4_t acc[QPK];
-#pragma unroll
-          for (int h = 0; h < QPK; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (!(pb & (1 << (w - 1)))) continue;
+          const uint32_t am = wa == (uint32_t)w ? 0xFFFFFFFFu : 0u;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[0] = mfma_bf16(as_bf16x8(QPK == 1 ? av[cb][i] : (av[cb][i] & hmask0)), as_bf16x8(W[w - 1][i]), acc[0]);
-            if (QPK == 2) acc[QPK - 1] = mfma_bf16(as_bf16x8(av[cb][i] & hmask1), as_bf16x8(W[w - 1][i]), acc[QPK - 1]);
-          }
+            const u32x4_t x0 = av[cb][i] & (am & hmask0);
+            const u32x4_t x1 = av[cb][i] & (am & hmask1);
 #pragma unroll
-          for (int h = 0; h < QPK; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[t][b][i] += o.s[t][h] * acc[h][i];
-        }
-        if (pb & (pb - 1)) {  // uniform: several widths
-          f32x4_t acc[QPK];
-#pragma unroll
-          for (int h = 0; h < QPK; ++h) acc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          // the widths are re-read here so that their comparisons are not
-          // kept live across the stream
-          const uint32_t wa = (vconst(wda) >> (4 * b)) & 15u;
-#pragma unroll
-          for (int w = 4; w >= 1; --w) {
-            if (!(MASK & (1 << (w - 1)))) continue;
-            if (!(pb & (1 << (w - 1)))) continue;
-            const uint32_t am = wa == (uint32_t)w ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc[0] = mfma_bf16(as_bf16x8(av[cb][i] & (am & hmask0)), as_bf16x8(W[w - 1][i]), acc[0]);
-              if (QPK == 2)
-                acc[QPK - 1] = mfma_bf16(as_bf16x8(av[cb][i] & (am & hmask1)), as_bf16x8(W[w - 1][i]), acc[QPK - 1]);
+            for (int t = 0; t < TP; ++t) {
+              acc[t][0] = mfma_bf16(as_bf16x8(x0), as_bf16x8(W[t][w - 1][i]), acc[t][0]);
+              if (QPK == 2) acc[t][QPK - 1] = mfma_bf16(as_bf16x8(x1), as_bf16x8(W[t][w - 1][i]), acc[t][QPK - 1]);
             }
           }
+        }
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
 #pragma unroll
           for (int h = 0; h < QPK; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[t][b][i] += o.s[t][h] * acc[h][i];
-        }
+            for (int i = 0; i < 4; ++i) out[t0 + t][b][i] += o.s[t0 + t][h] * acc[t][h][i];
       }
+    }
     }
     if (kb % SPB == SPB - 1 || kb == NKB - 1) {
 #pragma unroll
