@@ -14,18 +14,21 @@ its allocation and plan run as one single-block kernel, with the top-k too
 for T <= 16) on T=32 tokens at target 3.0 bits, replayed from HIP graphs
 that each hold one cycle of the 8 activation batches; a sweep over T in
 {1, 32} and targets {2.0, 2.5, 3.0, 4.0} follows.
-The roofline object is for the FFN stage (moe_anyprec_ffn: plan, activation
-gather, gate/up + SwiGLU, down, combine), timed with HIP events on its
-stream around each call, against the algorithmic bytes of that call.  Its
-"traffic" is the counter-measured HBM bytes per call recorded under
-profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy), used only
-while the kernel sources still hash to the value recorded there.
+The roofline object is for the FFN stage's dominant kernel, gate/up +
+SwiGLU, timed with HIP events recorded on the FFN's stream around that
+kernel's launch (moe_set_kernel_events), against its algorithmic bytes per
+launch; the down kernel and the whole FFN call are reported beside it.  Its
+"traffic" is the counter-measured HBM bytes per launch of that kernel
+recorded under profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated on a plain
+copy), used only while the kernel sources still hash to the value recorded
+there.
 
 With --prefill the same layer runs one T=4096 prefill batch with a
 Zipf(1.1)-skewed expert load (the grouped matrix-core path: chunks of 64
-pairs); that line's roofline is matrix-core bound, in TFLOP/s of the
-routed experts' SwiGLU FFN (6 d f flops per routed pair) against the bf16
-dense peak.
+pairs); that line's roofline is matrix-core bound: the gate/up kernel's
+algorithmic flops (4 d f per routed pair) over its event-timed duration,
+in TFLOP/s against the bf16 dense peak, the down kernel and the whole
+routed SwiGLU FFN (6 d f flops per routed pair) beside it.
 
 With --calibrated the widths come from a gate threshold calibrated once
 (MatMoE's calibration-threshold mode): the bisection runs over the gates of
@@ -104,6 +107,7 @@ def kernel_bytes(idx, bits, cfg, accumulate=False, expert_widths=None):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_qwen_T32_b3.0_hbm_bytes.md")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_prefill_qwen_T4096_counters.md")
 FFN_SOURCES = ("ffn.hip", "permute.hip", "common.hpp", "kernels.hpp")
 
 
@@ -115,13 +119,14 @@ def ffn_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(T, target):
-    """Counter-measured bytes per FFN call for the T=32, 3.0-bit decode
-    workload, or None when that record is missing or older than the kernels."""
-    if T != 32 or target != 3.0 or not os.path.exists(TRAFFIC_FILE):
+def recorded_traffic(T, target, path=TRAFFIC_FILE, T_rec=32):
+    """Counter-measured bytes per launch of the gate/up kernel for the
+    recorded workload (decode T=32 or prefill T=4096, 3.0 bits), or None when
+    that record is missing or older than the kernels."""
+    if T != T_rec or target != 3.0 or not os.path.exists(path):
         return None
     rec = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and not line.startswith(("|", "#", "`")):
                 k, v = line.split(":", 1)
@@ -524,6 +529,11 @@ def prefill(args, torch, bd, wl):
     t_step = L.timed_graph(args.target, args.steps, args.warmup)
     ev = L.timed_events(args.target, args.steps)
     tflops = ev["ffn_flops"] / (ev["ffn_ms"] * 1e-3) / 1e12
+    f13 = ev["ffn_flops"] * 2.0 / 3.0   # gate and up: 4 d f of the 6 d f per pair
+    t13 = f13 / (ev["w13_ms"] * 1e-3) / 1e12
+    t2 = (ev["ffn_flops"] - f13) / (ev["w2_ms"] * 1e-3) / 1e12
+    log(f"gate/up {ev['w13_ms'] * 1e3:.1f} us ({t13:.0f} TFLOP/s), down {ev['w2_ms'] * 1e3:.1f} us, "
+        f"FFN call {ev['ffn_ms'] * 1e3:.1f} us ({tflops:.0f} TFLOP/s)")
     ceiling = read_ceiling(torch, bd)
     out = {
         "metric": "MoE-layer tokens/s, prefill (Qwen3-30B shape)",
@@ -546,10 +556,17 @@ def prefill(args, torch, bd, wl):
         "bits_alloc": ev["bits_alloc"],
         "n_active_experts": ev["n_active"],
         "ffn_ms": {"mean": ev["ffn_ms"], "p10": ev["ffn_ms_p10"], "p50": ev["ffn_ms_p50"], "p90": ev["ffn_ms_p90"]},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "moe_anyprec_ffn (plan, gather, gate/up + SwiGLU, down, combine)",
-                     "flops_per_launch": ev["ffn_flops"], "hbm_gbs": ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": t13, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": t13 / BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(T, args.target, PREFILL_TRAFFIC_FILE, 4096),
+                     "kernel": "gate/up + SwiGLU on 64-pair chunks (k_wide<W13>), the FFN stage's dominant kernel",
+                     "flops_per_launch": f13, "us_per_launch": ev["w13_ms"] * 1e3,
+                     "down_kernel": {"achieved": t2, "frac": t2 / BF16_PEAK_TFLOPS,
+                                     "flops_per_launch": ev["ffn_flops"] - f13, "us_per_launch": ev["w2_ms"] * 1e3},
+                     "ffn_call": {"achieved": tflops, "frac": tflops / BF16_PEAK_TFLOPS,
+                                  "flops_per_launch": ev["ffn_flops"], "us_per_launch": ev["ffn_ms"] * 1e3,
+                                  "kernels": "plan, gather, gate/up + SwiGLU, group sums, down, combine",
+                                  "hbm_gbs": ev["ffn_bytes"] / (ev["ffn_ms"] * 1e-3) / 1e9},
                      "hbm_read_ceiling_gbs": ceiling},
         "cpu_baseline": None,
     }
