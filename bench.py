@@ -119,10 +119,11 @@ def ffn_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(T, target, path=TRAFFIC_FILE, T_rec=32):
+def recorded_traffic(T, target, path=None, T_rec=32):
     """Counter-measured bytes per launch of the gate/up kernel for the
     recorded workload (decode T=32 or prefill T=4096, 3.0 bits), or None when
     that record is missing or older than the kernels."""
+    path = TRAFFIC_FILE if path is None else path
     if T != T_rec or target != 3.0 or not os.path.exists(path):
         return None
     rec = {}

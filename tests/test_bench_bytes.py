@@ -48,6 +48,11 @@ def test_recorded_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.recorded_traffic(32, 2.5) is None
     rec.write_text("source_sha256: 0000000000000000\ntraffic_bytes_per_launch: 12345\n")
     assert bench.recorded_traffic(32, 3.0) is None
+    # the prefill record: its own file and token count
+    pre = tmp_path / "pre.md"
+    pre.write_text(f"source_sha256: {bench.ffn_source_hash()}\ntraffic_bytes_per_launch: 777\n")
+    assert bench.recorded_traffic(4096, 3.0, str(pre), 4096) == 777.0
+    assert bench.recorded_traffic(32, 3.0, str(pre), 4096) is None
 
 
 def test_bench_refuses_more_than_one_gpu():
