@@ -29,19 +29,24 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Block-wide sum of one count per thread.  Successive calls alternate
+// between two halves of `red` (2 x NT/64 ints), so one barrier per call
+// suffices: a half is written again only two calls later, after every thread
+// has passed the barrier of the call in between.
 template <int NT>
-__device__ __forceinline__ int block_count(int c, int* red) {
+__device__ __forceinline__ int block_count(int c, int* red, int& parity) {
   c = wave_sum_i_dpp(c);
   if constexpr (NT == WAVE) {
     return c;
   } else {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    __syncthreads();
-    if (lane == 0) red[wave] = c;
+    int* r = red + parity * (NT / WAVE);
+    parity ^= 1;
+    if (lane == 0) r[wave] = c;
     __syncthreads();
     int tot = 0;
 #pragma unroll
-    for (int w = 0; w < NT / WAVE; ++w) tot += red[w];
+    for (int w = 0; w < NT / WAVE; ++w) tot += r[w];
     return tot;
   }
 }
@@ -50,7 +55,8 @@ template <int NT, int AL_VPT>
 __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, int P, int n_star, int b_lo,
                                               int b_max, uint8_t* __restrict__ bits, float* __restrict__ tau_out,
                                               int* __restrict__ n_hi_out) {
-  __shared__ int red[NT / WAVE];
+  __shared__ int red[2 * (NT / WAVE)];
+  int parity = 0;
   const int tid = threadIdx.x;
   uint32_t keys[AL_VPT];
 #pragma unroll
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, in
 #pragma unroll
     for (int i = 0; i < AL_VPT; ++i) c += (keys[i] > cand) ? 1 : 0;
     for (int idx = in_regs + tid; idx < P; idx += NT) c += (order_key(gate[idx]) > cand) ? 1 : 0;
-    return block_count<NT>(c, red);
+    return block_count<NT>(c, red, parity);
   };
 
   uint32_t prefix = 0u;

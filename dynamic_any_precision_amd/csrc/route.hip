@@ -147,27 +147,43 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __res
   const int t = t0 + r16, e = e0 + r16;
   const uint16_t* xr = x + (size_t)(t < T ? t : 0) * d + 4 * q;
   const float* wr = W + (size_t)(e < E ? e : 0) * d + 4 * q;
-  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-  uint2 xa = t < T ? *reinterpret_cast<const uint2*>(xr) : make_uint2(0u, 0u);
-  float4 wb = e < E ? *reinterpret_cast<const float4*>(wr) : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < d; k0 += 16) {
-    const uint2 xc = xa;
-    const float4 wc = wb;
-    if (k0 + 16 < d) {
-      xa = t < T ? *reinterpret_cast<const uint2*>(xr + k0 + 16) : make_uint2(0u, 0u);
-      wb = e < E ? *reinterpret_cast<const float4*>(wr + k0 + 16) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // RING steps of 16 columns in flight (each wave's loads are a chain of
+  // dependent round trips otherwise); two accumulators alternate by step.
+  constexpr int RING = 4;
+  f64x4_t acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  uint2 xq[RING];
+  float4 wq[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) {
+    const int kk = 16 * r;
+    xq[r] = (t < T && kk < d) ? *reinterpret_cast<const uint2*>(xr + kk) : make_uint2(0u, 0u);
+    wq[r] = (e < E && kk < d) ? *reinterpret_cast<const float4*>(wr + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int k0 = 0; k0 < d; k0 += 16 * RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const uint2 xc = xq[r];
+      const float4 wc = wq[r];
+      const int kn = k0 + 16 * (r + RING);
+      if (kn < d) {
+        xq[r] = t < T ? *reinterpret_cast<const uint2*>(xr + kn) : make_uint2(0u, 0u);
+        wq[r] = e < E ? *reinterpret_cast<const float4*>(wr + kn) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (k0 + 16 * r < d) {
+        f64x4_t& a = acc[r & 1];
+        a = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x & 0xFFFFu), (double)wc.x, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x >> 16), (double)wc.y, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y & 0xFFFFu), (double)wc.z, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y >> 16), (double)wc.w, a, 0, 0, 0);
+      }
     }
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x & 0xFFFFu), (double)wc.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.x >> 16), (double)wc.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y & 0xFFFFu), (double)wc.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_to_f32(xc.y >> 16), (double)wc.w, acc, 0, 0, 0);
   }
   if (e < E) {
     const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = t0 + q + 4 * r;
-      if (tt < T) logits[(size_t)tt * E + e] = acc[r] + b;
+      if (tt < T) logits[(size_t)tt * E + e] = (acc[0][r] + acc[1][r]) + b;
     }
   }
 }
