@@ -10,7 +10,7 @@
 // most significant bit down: bit b of the answer is 0 iff
 // #{key > prefix | (2^b - 1)} <= n*, which makes tau the smallest key whose
 // strict upper set fits the budget.  32 steps, each one count reduced with
-// DPP lane moves (plus one LDS exchange between waves for large P).
+// DPP lane moves.  Larger batches take four radix passes instead (below).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -94,6 +94,84 @@ __global__ __launch_bounds__(NT) void k_alloc(const float* __restrict__ gate, in
   }
 }
 
+// Large batches: the same tau by a radix descent over 8-bit digits instead of
+// 32 bisection steps.  In each of four passes the keys that share the prefix
+// found so far are histogrammed by their next digit, and the digit becomes
+// the smallest d for which the keys above the prefix plus the prefix's keys
+// with a digit above d number at most n*.  This is the smallest 32-bit value
+// whose strict upper set fits the budget, the bisection's answer.
+template <int NT, int AL_VPT>
+__global__ __launch_bounds__(NT) void k_alloc_radix(const float* __restrict__ gate, int P, int n_star, int b_lo,
+                                                    int b_max, uint8_t* __restrict__ bits, float* __restrict__ tau_out,
+                                                    int* __restrict__ n_hi_out) {
+  __shared__ int hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_above;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t keys[AL_VPT];
+#pragma unroll
+  for (int i = 0; i < AL_VPT; ++i) {
+    const int idx = tid + i * NT;
+    keys[i] = idx < P ? order_key(gate[idx]) : 0u;
+  }
+  const int in_regs = NT * AL_VPT;
+  uint32_t prefix = 0u;
+  int above = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int j = tid; j < 256; j += NT) hist[j] = 0;
+    __syncthreads();
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int i = 0; i < AL_VPT; ++i)
+      if (tid + i * NT < P && (keys[i] & hmask) == prefix) atomicAdd(&hist[(keys[i] >> shift) & 255u], 1);
+    for (int idx = in_regs + tid; idx < P; idx += NT) {
+      const uint32_t k = order_key(gate[idx]);
+      if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int ls = h0 + h1 + h2 + h3;
+      int suf = ls;  // sum over lanes >= this one
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_down(suf, m, WAVE);
+        if (lane + m < 64) suf += o;
+      }
+      // the prefix's keys with a digit above 4 lane + i
+      int sd[4];
+      sd[3] = suf - ls;
+      sd[2] = sd[3] + h3;
+      sd[1] = sd[2] + h2;
+      sd[0] = sd[1] + h1;
+      int dmin = 256;
+#pragma unroll
+      for (int i = 3; i >= 0; --i)
+        if (above + sd[i] <= n_star) dmin = 4 * lane + i;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) dmin = min(dmin, __shfl_xor(dmin, m, WAVE));
+      if (lane == (dmin >> 2)) {
+        s_prefix = prefix | ((uint32_t)dmin << shift);
+        s_above = above + sd[dmin & 3];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    above = s_above;
+  }
+#pragma unroll
+  for (int i = 0; i < AL_VPT; ++i) {
+    const int idx = tid + i * NT;
+    if (idx < P) bits[idx] = (uint8_t)(keys[i] > prefix ? b_max : b_lo);
+  }
+  for (int idx = in_regs + tid; idx < P; idx += NT)
+    bits[idx] = (uint8_t)(order_key(gate[idx]) > prefix ? b_max : b_lo);
+  if (tid == 0) {
+    if (tau_out) *tau_out = (n_star >= P) ? -INFINITY : key_to_float(prefix);
+    if (n_hi_out) *n_hi_out = above;
+  }
+}
+
 // Fixed-threshold widths (calibration-threshold mode): one thread per pair.
 __global__ __launch_bounds__(256) void k_bits_threshold(const float* __restrict__ gate, int P, float tau, int b_lo,
                                                         int b_max, uint8_t* __restrict__ bits) {
@@ -135,7 +213,7 @@ hipError_t launch_alloc(const float* gate, int P, int n_star, int b_lo, int b_ma
     hipLaunchKernelGGL((k_alloc<WAVE, 32>), dim3(1), dim3(WAVE), 0, stream, gate, P, n_star, b_lo, b_max, bits,
                        tau_out, n_hi_out);
   } else {
-    hipLaunchKernelGGL((k_alloc<1024, 32>), dim3(1), dim3(1024), 0, stream, gate, P, n_star, b_lo, b_max, bits,
+    hipLaunchKernelGGL((k_alloc_radix<1024, 32>), dim3(1), dim3(1024), 0, stream, gate, P, n_star, b_lo, b_max, bits,
                        tau_out, n_hi_out);
   }
   return hipGetLastError();

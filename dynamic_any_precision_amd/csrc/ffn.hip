@@ -217,9 +217,14 @@ struct GatherArgs {
   float2* xvg;
 };
 
+// GKB k-blocks per block, their row loads all issued first: four for 64-pair
+// chunks, one for 16-pair chunks (more and smaller blocks)
+template <int GKB>
 __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   const int c = blockIdx.x;  // 16-token block: chunk c / sub, block c % sub of it
-  const int kb = blockIdx.y;
+  const int kb0 = blockIdx.y * GKB;
+  const int nkb = a.d / 128;
+  const int kb1 = kb0 + GKB < nkb ? kb0 + GKB : nkb;
   const int ck = c / a.sub;
   // the chunk record is loaded with the routed chunk count, not after it
   // (every record index is inside the chunk array)
@@ -228,43 +233,56 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   if (ck < a.max_rchunks && ck >= nrc) return;
   const int s0 = ch.y + 16 * (c - ck * a.sub), m = ch.z - 16 * (c - ck * a.sub);
   const int tid = threadIdx.x, t = tid >> 4, q = tid & 15;
-  __shared__ uint4 frag[256];
-  uint16_t* fr = reinterpret_cast<uint16_t*>(frag);
-  uint32_t in[4] = {0u, 0u, 0u, 0u};
-  if (t < m) {
-    const int tok = a.slot_info[s0 + t] & 0xFFFFFF;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.x + (size_t)tok * a.d + kb * 128 + 8 * q);
-    in[0] = v.x; in[1] = v.y; in[2] = v.z; in[3] = v.w;
-  }
-  float X = 0.f, V = 0.f;
+  __shared__ uint4 frag[GKB][256];
+  uint32_t in[GKB][4];
+  const int tok = t < m ? (a.slot_info[s0 + t] & 0xFFFFFF) : 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int col = 8 * q + j;  // column within the k-block
-    const int cc = col & 31;
-    const float xf = bf16_to_f32((j & 1) ? (in[j >> 1] >> 16) : (in[j >> 1] & 0xFFFFu));
-    // 4^-a for the plane-unit operands of 16-pair chunks, 8^-a for the
-    // nibble operands of 64-pair chunks
-    const float sc = a.sub > 1 ? 1.0f / (float)(1 << (3 * a_nib(cc & 15))) : 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
-    X += xf;
-    V += xf * sc;
-    const int fp = frag_pos(cc);
-    fr[((fp >> 3) * 64 + (col >> 5) * 16 + t) * 8 + (fp & 7)] = (uint16_t)f32_to_bf16(xf * sc);
+  for (int g = 0; g < GKB; ++g) {
+    const int kb = kb0 + g;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t < m && kb < kb1) v = *reinterpret_cast<const uint4*>(a.x + (size_t)tok * a.d + kb * 128 + 8 * q);
+    in[g][0] = v.x; in[g][1] = v.y; in[g][2] = v.z; in[g][3] = v.w;
   }
   const int tpg = a.g >> 3;  // threads per quant group
-  for (int msk = 1; msk < tpg; msk <<= 1) {
-    X += __shfl_xor(X, msk, WAVE);
-    V += __shfl_xor(V, msk, WAVE);
-  }
   const int NQG = a.d / a.g;
   // 16-pair chunks: rows past the chunk's pairs are never read (the FFN
   // loads them as out-of-range, i.e. zero), so only live rows are written;
   // 64-pair chunks copy whole blocks and get zero rows.
   const bool live = a.sub > 1 || t < m;
-  if ((q & (tpg - 1)) == 0 && live)
-    a.xvg[((size_t)c * NQG + kb * (128 / a.g) + q / tpg) * 16 + t] = make_float2(X, V);
+#pragma unroll
+  for (int g = 0; g < GKB; ++g) {
+    const int kb = kb0 + g;
+    if (kb >= kb1) break;
+    uint16_t* fr = reinterpret_cast<uint16_t*>(frag[g]);
+    float X = 0.f, V = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = 8 * q + j;  // column within the k-block
+      const int cc = col & 31;
+      const float xf = bf16_to_f32((j & 1) ? (in[g][j >> 1] >> 16) : (in[g][j >> 1] & 0xFFFFu));
+      // 4^-a for the plane-unit operands of 16-pair chunks, 8^-a for the
+      // nibble operands of 64-pair chunks
+      const float sc = a.sub > 1 ? 1.0f / (float)(1 << (3 * a_nib(cc & 15))) : 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+      X += xf;
+      V += xf * sc;
+      const int fp = frag_pos(cc);
+      fr[((fp >> 3) * 64 + (col >> 5) * 16 + t) * 8 + (fp & 7)] = (uint16_t)f32_to_bf16(xf * sc);
+    }
+    for (int msk = 1; msk < tpg; msk <<= 1) {
+      X += __shfl_xor(X, msk, WAVE);
+      V += __shfl_xor(V, msk, WAVE);
+    }
+    if ((q & (tpg - 1)) == 0 && live)
+      a.xvg[((size_t)c * NQG + kb * (128 / a.g) + q / tpg) * 16 + t] = make_float2(X, V);
+  }
   __syncthreads();
-  if (a.sub > 1 || (tid & 15) < m)
-    reinterpret_cast<uint4*>(a.xg + ((size_t)c * (a.d / 128) + kb) * 2048)[tid] = frag[tid];
+#pragma unroll
+  for (int g = 0; g < GKB; ++g) {
+    const int kb = kb0 + g;
+    if (kb >= kb1) break;
+    if (a.sub > 1 || (tid & 15) < m)
+      reinterpret_cast<uint4*>(a.xg + ((size_t)c * nkb + kb) * 2048)[tid] = frag[g][tid];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1709,7 +1727,11 @@ hipError_t launch_gather(const FfnShape& s, const FfnLayout& L, char* ws, const 
   a.slot_info = reinterpret_cast<const int*>(ws + L.slot_info);
   a.xg = reinterpret_cast<uint16_t*>(ws + L.xg);
   a.xvg = reinterpret_cast<float2*>(ws + L.xvg);
-  hipLaunchKernelGGL(k_gather, dim3((s.max_rchunks + s.n_schunks) * s.sub, s.d / 128), dim3(256), 0, stream, a);
+  const int nb = (s.max_rchunks + s.n_schunks) * s.sub, nkb = s.d / 128;
+  if (s.sub > 1)
+    hipLaunchKernelGGL(k_gather<4>, dim3(nb, (nkb + 3) / 4), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_gather<1>, dim3(nb, nkb), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
