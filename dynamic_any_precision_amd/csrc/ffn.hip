@@ -770,9 +770,7 @@ __global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn
 // tokens: at T = 1 the gate/up step has 8 x 48 items for 2048 wave slots),
 // each wave of the whole-K kernel above streams its item's 16 k-blocks as one
 // dependent chain.  Here each item gets a workgroup and its k-blocks are cut
-// four ways; the partial sums meet in LDS.
-
-constexpr int KS_WAVES = 4;
+// two or four ways; the partial sums meet in LDS.
 
 template <int MODE, int QPK, int MASK>
 __device__ __forceinline__ void stream_part(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
@@ -1122,13 +1120,13 @@ __device__ __forceinline__ void sk_stream(const FfnArgs& a, const SkItem& it, in
   }
 }
 
-// One item per workgroup, its k-blocks split over the four waves (wave q
-// streams k-blocks [q K/4, (q+1) K/4) of the item); wave 0 adds the four
-// partial sums from LDS in wave order and finishes the item.  Workgroup b
+// One item per workgroup, its k-blocks split over the KS_WAVES waves (wave q
+// streams k-blocks [q K/KS_WAVES, (q+1) K/KS_WAVES) of the item); wave 0 adds
+// the partial sums from LDS in wave order and finishes the item.  Workgroup b
 // takes item b (an XCD-aware order keeps a chunk's items on one XCD); the
 // items past the call's routed chunks leave at once.
-template <int MODE, int QPK>
-__global__ __launch_bounds__(FFN_THREADS) __attribute__((amdgpu_waves_per_eu(ffn_wpe(MODE, QPK), ffn_wpe(MODE, QPK)))) void k_ffn_small(FfnArgs a) {
+template <int MODE, int QPK, int KS_WAVES>
+__global__ __launch_bounds__(64 * KS_WAVES) __attribute__((amdgpu_waves_per_eu(ffn_wpe(MODE, QPK), ffn_wpe(MODE, QPK)))) void k_ffn_small(FfnArgs a) {
   __shared__ f32x4_t part[KS_WAVES][2][64];
   const int wave = uniform((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1679,18 +1677,28 @@ hipError_t launch_ffn(int mode, const FfnShape& s, const FfnLayout& L, char* ws,
   const long max_items = (long)s.max_rchunks * a.items[0] + (long)s.n_schunks * a.items[1];
   if (max_items <= (long)num_cu * ffn_wpe(mode, qpk) * 2) {
     // at most one item per two wave slots: one workgroup per item, its
-    // k-blocks split over the workgroup's four waves
+    // k-blocks split over the workgroup's waves: four while the items fill at
+    // most 2.5 workgroups per CU, else two (more items, shorter chains
+    // already)
     const int nwg = (int)((max_items + 7) & ~7L);
+    const bool ks4 = max_items * 4 <= (long)num_cu * 10;
+    const dim3 g(nwg);
     if (mode == MODE_W13) {
-      if (qpk == 2)
-        hipLaunchKernelGGL((k_ffn_small<MODE_W13, 2>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
-      else
-        hipLaunchKernelGGL((k_ffn_small<MODE_W13, 1>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+      if (qpk == 2) {
+        if (ks4) hipLaunchKernelGGL((k_ffn_small<MODE_W13, 2, 4>), g, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_ffn_small<MODE_W13, 2, 2>), g, dim3(128), 0, stream, a);
+      } else {
+        if (ks4) hipLaunchKernelGGL((k_ffn_small<MODE_W13, 1, 4>), g, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_ffn_small<MODE_W13, 1, 2>), g, dim3(128), 0, stream, a);
+      }
     } else {
-      if (qpk == 2)
-        hipLaunchKernelGGL((k_ffn_small<MODE_W2, 2>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
-      else
-        hipLaunchKernelGGL((k_ffn_small<MODE_W2, 1>), dim3(nwg), dim3(FFN_THREADS), 0, stream, a);
+      if (qpk == 2) {
+        if (ks4) hipLaunchKernelGGL((k_ffn_small<MODE_W2, 2, 4>), g, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_ffn_small<MODE_W2, 2, 2>), g, dim3(128), 0, stream, a);
+      } else {
+        if (ks4) hipLaunchKernelGGL((k_ffn_small<MODE_W2, 1, 4>), g, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_ffn_small<MODE_W2, 1, 2>), g, dim3(128), 0, stream, a);
+      }
     }
     return hipGetLastError();
   }
