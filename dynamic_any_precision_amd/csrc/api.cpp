@@ -122,7 +122,8 @@ hipError_t ffn_after_plan(const moe::FfnShape& s, const moe::FfnLayout& L, char*
   std::memset(&none, 0, sizeof(none));
   none.N = 16;
   none.K = 128;
-  hipError_t e = moe::launch_gather(s, L, ws, x, strm);
+  // one token: the plan kernel wrote the token's fragment, which every chunk reads
+  hipError_t e = s.act_shared ? hipSuccess : moe::launch_gather(s, L, ws, x, strm);
   if (e == hipSuccess) e = mark(0, strm);
   if (e == hipSuccess)
     e = moe::launch_ffn_w13(s, L, ws, w13_of(routed), shared ? w13_of(shared) : none, ncu, strm);
@@ -240,7 +241,14 @@ moe_status moe_anyprec_ffn(const moe_expert_bank* routed, const moe_expert_bank*
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
+  hipError_t e;
+  if (moe::one_token_fits(s)) {
+    s.act_shared = 1;
+    e = moe::launch_one(s, L, ws, x, nullptr, 0, 0, 0, 0, const_cast<int32_t*>(topk_idx), nullptr,
+                        const_cast<uint8_t*>(bits), strm);
+  } else {
+    e = moe::launch_plan(s, L, ws, topk_idx, bits, strm);
+  }
   if (e == hipSuccess) e = ffn_after_plan(s, L, ws, routed, shared, x, topk_gate, y, accumulate, strm);
   return hip_status(e);
 }
@@ -275,7 +283,10 @@ moe_status moe_layer(const moe_expert_bank* routed, const moe_expert_bank* share
   const int32_t n_star = exact_budget(s.P, b_lo, b_max, target_avg_bits);
   hipError_t e = moe::launch_route_logits(x, T, s.d, w_router, s.E, logit_bias, logits, strm);
   if (e == hipSuccess) {
-    if (moe::control_fits(s)) {
+    if (moe::one_token_fits(s)) {
+      s.act_shared = 1;
+      e = moe::launch_one(s, L, ws, x, logits, renorm_topk, n_star, b_lo, b_max, topk_idx, topk_gate, bits, strm);
+    } else if (moe::control_fits(s)) {
       if (!moe::control_does_topk(s))
         e = moe::launch_route_topk(logits, T, s.E, top_k, renorm_topk, topk_idx, topk_gate, strm);
       if (e == hipSuccess)

@@ -204,6 +204,16 @@ __host__ __device__ __forceinline__ void unpack_nib(uint32_t n3, uint32_t n2, ui
   }
 }
 
+// Place of lane (token row r16, k-chunk jg) inside the 1 KiB operand block of
+// one matrix-core product, for the streaming kernels' activations.  Gate/up
+// (gathered token rows of 16-pair chunks): token-major, r16 * 4 + jg, so the
+// live rows of a chunk (the first m) are one contiguous 64 m bytes and a
+// load touches m/2 cache lines instead of four separate 256-byte stretches.
+// Down (the SwiGLU output h): k-chunk-major, jg * 16 + r16 = lane.
+__device__ __forceinline__ uint32_t act_pos(int mode, int r16, int jg) {
+  return mode == 0 ? (uint32_t)(r16 * 4 + jg) : (uint32_t)(jg * 16 + r16);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ u32x4_t as_u32x4(uint4 v) { return u32x4_t{v.x, v.y, v.z, v.w}; }

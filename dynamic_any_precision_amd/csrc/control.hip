@@ -198,6 +198,153 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
   plan_small_core(s, pp, L, 0);
 }
 
+
+// One token (T = 1).  Every routed expert then holds at most one pair, so each
+// valid pair is a chunk of its own and its slot is its rank in the (expert,
+// width) key order of the general plan, and every chunk reads the same token
+// row: the token's activation fragment is written once, as chunk 0's, and the
+// streaming kernels are told to read it for every chunk.  One block:
+//   1. all threads: the fragment (the gather's arithmetic, per 16 k-blocks);
+//   2. wave 0: with logits, the top-k (the top-k kernel's arithmetic) and the
+//      allocation of the k pairs (high width iff #{keys >= own key} <= n*, as
+//      in the fused control kernel); without, the given experts and widths;
+//      then the dropping rules, slots and chunk records of the general plan;
+//   3. all threads: expert offsets and widest widths.
+constexpr int ONE_NT = 256;
+
+__global__ __launch_bounds__(ONE_NT) void k_one(FfnShape s, PlanPtrs pp, const uint16_t* __restrict__ x,
+                                                uint16_t* __restrict__ xg, float2* __restrict__ xvg,
+                                                const double* __restrict__ logits, int renorm, int n_star, int b_lo,
+                                                int b_max, int* __restrict__ idx, float* __restrict__ gate,
+                                                uint8_t* __restrict__ bits) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint4 fr[16][16];  // per k-block of a pass: the 16 operand uint4 of the token's row
+  __shared__ int s_e[8], s_w[8];       // per pair: expert (-1: dropped) and width
+  const int nkb = s.d / 128, tpg = s.g >> 3;
+
+  // 1. activation fragment of the token, chunk 0's place
+  {
+    const int kbl = tid >> 4, q = tid & 15;
+    for (int kb0 = 0; kb0 < nkb; kb0 += 16) {
+      const int kb = kb0 + kbl;
+      const bool on = kb < nkb;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (on) v = *reinterpret_cast<const uint4*>(x + kb * 128 + 8 * q);
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+      float X = 0.f, V = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = 8 * q + j;
+        const int cc = col & 31;
+        const float xf = bf16_to_f32((j & 1) ? (in[j >> 1] >> 16) : (in[j >> 1] & 0xFFFFu));
+        const float sc = 1.0f / (float)(1 << (2 * a_exp(cc & 15)));
+        X += xf;
+        V += xf * sc;
+        const int fp = frag_pos(cc);
+        reinterpret_cast<uint16_t*>(fr[kbl])[((fp >> 3) * 4 + (col >> 5)) * 8 + (fp & 7)] =
+            (uint16_t)f32_to_bf16(xf * sc);
+      }
+      for (int msk = 1; msk < tpg; msk <<= 1) {
+        X += __shfl_xor(X, msk, WAVE);
+        V += __shfl_xor(V, msk, WAVE);
+      }
+      if (on && (q & (tpg - 1)) == 0) xvg[(size_t)(kb * (128 / s.g) + q / tpg) * 16] = make_float2(X, V);
+      __syncthreads();
+      if (on) {
+        const int i = q >> 2, jg = q & 3;
+        reinterpret_cast<uint4*>(xg)[(size_t)kb * 256 + i * 64 + act_pos(0, 0, jg)] =
+            fr[kbl][q];
+      }
+      __syncthreads();
+    }
+  }
+
+  // 2. routing, widths and the plan of the k pairs (lane j: pair j)
+  if (wave == 0) {
+    const int k = s.k, B = s.B;
+    int e = -1, b = 0;
+    if (logits) {
+      float g = 0.f;
+      topk_token(logits, s.E, k, renorm, [&](int j, int ex, float gv) {
+        idx[j] = ex;
+        gate[j] = gv;
+        e = ex;
+        g = gv;
+      }, lane);
+      const uint32_t key = lane < k ? gate_key(g) : 0u;
+      int ge = 0;
+      for (int r = 0; r < k; ++r) ge += ((uint32_t)__builtin_amdgcn_readlane((int)key, r) >= key) ? 1 : 0;
+      b = ge <= n_star ? b_max : b_lo;
+      if (lane < k) bits[lane] = (uint8_t)b;
+    } else if (lane < k) {
+      e = idx[lane];
+      b = bits[lane];
+    }
+    // dropped: an expert or width out of range, or an expert an earlier pair
+    // of the token (with a width in range) already has
+    int err = 0;
+    bool valid = lane < k;
+    if (valid && (e < 0 || e >= s.E || b < 1 || b > B)) {
+      err |= 1;
+      valid = false;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j), bj = __builtin_amdgcn_readlane(b, j);
+      if (valid && j < lane && ej == e && bj >= 1 && bj <= B) {
+        err |= 2;
+        valid = false;
+      }
+    }
+    const int w = valid ? clamp_width(s, e, b) : 0;
+    const int key = valid ? e * B + (B - w) : 0x7FFFFFFF;
+    int slot = 0, nvalid = 0, errs = 0;
+    for (int j = 0; j < k; ++j) {
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      slot += (kj < key) ? 1 : 0;
+      nvalid += (kj != 0x7FFFFFFF) ? 1 : 0;
+      errs |= __builtin_amdgcn_readlane(err, j);
+    }
+    if (lane < k) {
+      pp.pair_slot[lane] = valid ? slot : -1;
+      s_e[lane] = valid ? e : -1;
+      s_w[lane] = w;
+      if (valid) {
+        pp.slot_pair[slot] = lane;
+        pp.slot_info[slot] = w << 24;  // token 0
+        pp.chunks[slot] = make_int4(e, slot, 1, 1 << (w - 1));
+        int cnt = 0;
+        for (int bb = 1; bb <= w; ++bb) cnt |= 1 << (8 * (bb - 1));
+        pp.chunk_cnt[slot] = cnt;
+      }
+    }
+    if (lane >= nvalid && lane < s.P) pp.slot_pair[lane] = -1;
+    if (lane == 0) {
+      pp.meta[0] = nvalid;
+      pp.meta[1] = errs;
+    }
+    // shared experts: the token at full width
+    if (lane < s.n_shared) {
+      pp.chunks[s.max_rchunks + lane] = make_int4(lane, s.P + lane, 1, (1 << (B - 1)) | (1 << 16));
+      int cnt = 0;
+      for (int bb = 1; bb <= B; ++bb) cnt |= 1 << (8 * (bb - 1));
+      pp.chunk_cnt[s.max_rchunks + lane] = cnt;
+      pp.slot_info[s.P + lane] = B << 24;
+    }
+  }
+  __syncthreads();
+
+  // 3. expert offsets (valid pairs of smaller experts) and widest widths
+  for (int e = tid; e <= s.E; e += ONE_NT) {
+    int off = 0, mb = 0;
+    for (int j = 0; j < s.k; ++j) {
+      const int ej = s_e[j];
+      off += (ej >= 0 && ej < e) ? 1 : 0;
+      if (ej == e) mb = s_w[j];
+    }
+    pp.expert_off[e] = off;
+    if (e < s.E) pp.expert_maxbits[e] = mb;
+  }
+}
 }  // namespace
 
 bool control_fits(const FfnShape& s) {
@@ -216,6 +363,18 @@ hipError_t launch_control(const FfnShape& s, const FfnLayout& L, char* ws, const
   else
     hipLaunchKernelGGL(k_control<false>, dim3(1), dim3(PM_NT), 0, stream, s, plan_ptrs(L, ws), logits, renorm,
                        n_star, b_lo, b_max, idx, gate, bits);
+  return hipGetLastError();
+}
+
+
+bool one_token_fits(const FfnShape& s) { return s.T == 1 && s.cs == 16 && s.k <= 8 && s.n_shared <= 64; }
+
+hipError_t launch_one(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, const double* logits,
+                      int renorm, int n_star, int b_lo, int b_max, int* idx, float* gate, uint8_t* bits,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL(k_one, dim3(1), dim3(ONE_NT), 0, stream, s, plan_ptrs(L, ws), x,
+                     reinterpret_cast<uint16_t*>(ws + L.xg), reinterpret_cast<float2*>(ws + L.xvg), logits, renorm,
+                     n_star, b_lo, b_max, idx, gate, bits);
   return hipGetLastError();
 }
 

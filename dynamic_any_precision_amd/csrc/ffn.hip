@@ -56,6 +56,7 @@ FfnShape make_shape(int T, int k, int E, int B, int g, int d, int f, int n_share
   s.n_schunks = n_shared * ((T + s.cs - 1) / s.cs);
   s.fmax = s.fs > f ? s.fs : f;
   s.bprefix = nullptr;
+  s.act_shared = 0;
   return s;
 }
 
@@ -161,6 +162,7 @@ struct FfnArgs {
   const float2* asum;    // W13: (X, V) per [chunk][K/g][16]; W2: per [chunk][16][fmax/16]
   int act_stride;        // elements per chunk
   int asum_stride;       // float2 per chunk
+  int act_shared;        // gate/up: every chunk reads chunk 0's activations (one token: all chunks hold it)
   uint16_t* hg;          // gate/up output fragments, [chunk][fmax/128][4][64][8]
   float2* hsg;           // gate/up output partial sums [chunk][16][fmax/16]
   float2* hsgg;          // wide chunks: gate/up output group sums [block][fmax/g][16]
@@ -266,7 +268,8 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
       X += xf;
       V += xf * sc;
       const int fp = frag_pos(cc);
-      fr[((fp >> 3) * 64 + (col >> 5) * 16 + t) * 8 + (fp & 7)] = (uint16_t)f32_to_bf16(xf * sc);
+      const int pos = a.sub > 1 ? (col >> 5) * 16 + t : t * 4 + (col >> 5);
+      fr[((fp >> 3) * 64 + pos) * 8 + (fp & 7)] = (uint16_t)f32_to_bf16(xf * sc);
     }
     for (int msk = 1; msk < tpg; msk <<= 1) {
       X += __shfl_xor(X, msk, WAVE);
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   for (int g = 0; g < GKB; ++g) {
     const int kb = kb0 + g;
     if (kb >= kb1) break;
-    if (a.sub > 1 || (tid & 15) < m)
+    if (a.sub > 1 || ((tid & 63) >> 2) < m)
       reinterpret_cast<uint4*>(a.xg + ((size_t)c * nkb + kb) * 2048)[tid] = frag[g][tid];
   }
 }
@@ -395,14 +398,15 @@ __device__ __forceinline__ void run_item(const FfnArgs& a, const MatrixDev& M, c
       make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)c * a.act_stride, (uint32_t)K * 32);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)c * a.asum_stride, (uint32_t)a.asum_stride * 8);
+  const int ca = (MODE == MODE_W13 && a.act_shared) ? 0 : c;  // chunk whose activations this one reads
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)ca * a.act_stride, (uint32_t)K * 32);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)ca * a.asum_stride, (uint32_t)a.asum_stride * 8);
 
   // Per-lane offsets.  Group sums: gate/up reads (X, V) of one group of token
   // r16 in the lanes of that group's k-slot; down reads two of the 16-column
   // partial sums of token r16 per lane (group kb*QPK + (jg & (QPK - 1))).
   // activation rows past the chunk's pairs are zero: their lanes read nothing
-  const uint32_t vo_act = r16 < m ? lane * 16 : OOB;
+  const uint32_t vo_act = r16 < m ? act_pos(MODE, r16, jg) * 16 : OOB;
   const uint32_t vo_pl = lane * 4;
   const uint32_t vo_s = r16 * 4;
   // Gate/up collects the group terms of SPB = 4/QPK k-blocks in the four
@@ -819,10 +823,11 @@ __device__ __forceinline__ void stream_part(const FfnArgs& a, const MatrixDev& M
       make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
   const uint32_t sz_bytes = (uint32_t)((M.N >> 4) * NQG * 128);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(M.sz + (size_t)e * (sz_bytes / 4), sz_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)c * a.act_stride, (uint32_t)K * 32);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)c * a.asum_stride, (uint32_t)a.asum_stride * 8);
+  const int ca = (MODE == MODE_W13 && a.act_shared) ? 0 : c;  // chunk whose activations this one reads
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.act + (size_t)ca * a.act_stride, (uint32_t)K * 32);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.asum + (size_t)ca * a.asum_stride, (uint32_t)a.asum_stride * 8);
 
-  const uint32_t vo_act = r16 < m ? lane * 16 : OOB;
+  const uint32_t vo_act = r16 < m ? act_pos(MODE, r16, jg) * 16 : OOB;
   const uint32_t vo_pl = lane * 4;
   const uint32_t vo_s = r16 * 4;
   constexpr int SPB = 4 / QPK;
@@ -1622,6 +1627,7 @@ FfnArgs make_args(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev rou
   a.hsgg = reinterpret_cast<float2*>(ws + L.hsgg);
   a.sub = s.sub;
   a.bprefix = s.bprefix;
+  a.act_shared = s.act_shared;
   return a;
 }
 

@@ -40,6 +40,7 @@ struct FfnShape {
   int cs;                // pairs per chunk: 16 (decode), or 64 (prefill: four 16-token blocks)
   int sub;               // 16-token blocks per chunk (cs / 16)
   const int* bprefix;    // routed bank's per-expert plane prefix [E+1] (device), or null (uniform)
+  int act_shared;        // one token: the plan wrote one activation fragment that every chunk reads
 };
 
 struct FfnLayout {
@@ -69,6 +70,12 @@ bool control_does_topk(const FfnShape& s);
 hipError_t launch_control(const FfnShape& s, const FfnLayout& L, char* ws, const double* logits, int renorm,
                           int n_star, int b_lo, int b_max, int* idx, float* gate, uint8_t* bits,
                           hipStream_t stream);
+// One token: softmax + top-k (when logits is not null; else idx and bits are
+// inputs), allocation, plan and the token's activation fragment in one block.
+bool one_token_fits(const FfnShape& s);
+hipError_t launch_one(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, const double* logits,
+                      int renorm, int n_star, int b_lo, int b_max, int* idx, float* gate, uint8_t* bits,
+                      hipStream_t stream);
 // Activation fragments of every chunk (after the plan).
 hipError_t launch_gather(const FfnShape& s, const FfnLayout& L, char* ws, const uint16_t* x, hipStream_t stream);
 hipError_t launch_ffn_w13(const FfnShape& s, const FfnLayout& L, char* ws, MatrixDev routed, MatrixDev shared,

@@ -550,6 +550,36 @@ def test_ffn_drops_invalid_pairs():
     assert rel_l2(y.cpu().numpy(), ref) < REL_L2
 
 
+def test_ffn_one_token_drops_invalid_and_repeated():
+    # One token runs its own plan kernel (each pair a chunk of its own); it
+    # keeps the general plan's dropping rules: an expert out of range, a width
+    # out of range, a repeat of an earlier pair's expert (of a repeat, the
+    # first pair with a valid width is kept).
+    w, dev, oc, _ = workload(2)
+    cfg = w.cfg
+    x = dev["x"][:1].contiguous()
+    idx, gate = bd.route(x, dev["w_router"], dev["bias"], cfg.k)
+    bits = bd.alloc_bits(gate.reshape(-1), cfg.b_lo, 4, cfg.target)
+    idx_bad, bits_bad = idx.clone(), bits.clone()
+    idx_bad[0, 2] = idx[0, 1]   # repeats pair 1: dropped
+    idx_bad[0, 3] = idx[0, 4]   # pair 3 and pair 4 share an expert ...
+    bits_bad[3] = 9             # ... pair 3's width is out of range: dropped, pair 4 kept
+    idx_bad[0, 5] = 500         # expert out of range: dropped
+    bits_bad[6] = 0             # width out of range: dropped
+    note("ffn one token, invalid and repeated pairs")
+    y = bd.anyprec_ffn(dev["routed"], None, x, idx_bad, gate, bits_bad)
+    torch.cuda.synchronize()
+    g = gate.cpu().numpy().astype(np.float64)
+    g[0, [2, 3, 5, 6]] = 0.0
+    ref = orc.combine(w.x_bf16[:1], idx.cpu().numpy(), g, bits.cpu().numpy().astype(np.int64), oc)
+    err = rel_l2(y.cpu().numpy(), ref)
+    assert err < REL_L2, err
+    # accumulate onto y, one token, shared experts (DeepSeek shape, B_lo 1)
+    note("ffn one token accumulate cfg3 b_lo=1")
+    err, _ = _ffn_case(3, T=1, accumulate=True, over=dict(b_lo=1))
+    assert err < REL_L2, err
+
+
 @pytest.mark.parametrize("rows,d", [(64, 2048), (3, 100), (5, 1), (1, 4096)])
 def test_rmsnorm_to_bf16_exact(rows, d):
     # rows of very different magnitudes, a zero row, ragged widths
