@@ -204,7 +204,8 @@ __global__ __launch_bounds__(PM_NT) void k_control(FfnShape s, PlanPtrs pp, cons
 // width) key order of the general plan, and every chunk reads the same token
 // row: the token's activation fragment is written once, as chunk 0's, and the
 // streaming kernels are told to read it for every chunk.  One block:
-//   1. all threads: the fragment (the gather's arithmetic, per 16 k-blocks);
+//   1. waves 1-3: the fragment (the gather's arithmetic, four k-blocks per wave
+//      and pass), while
 //   2. wave 0: with logits, the top-k (the top-k kernel's arithmetic) and the
 //      allocation of the k pairs (high width iff #{keys >= own key} <= n*, as
 //      in the fused control kernel); without, the given experts and widths;
@@ -218,14 +219,16 @@ __global__ __launch_bounds__(ONE_NT) void k_one(FfnShape s, PlanPtrs pp, const u
                                                 int b_max, int* __restrict__ idx, float* __restrict__ gate,
                                                 uint8_t* __restrict__ bits) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ uint4 fr[16][16];  // per k-block of a pass: the 16 operand uint4 of the token's row
+  __shared__ uint4 fr[3][4][16];  // per fragment wave and k-block of a pass: the token row's 16 operand uint4
   __shared__ int s_e[8], s_w[8];       // per pair: expert (-1: dropped) and width
   const int nkb = s.d / 128, tpg = s.g >> 3;
 
-  // 1. activation fragment of the token, chunk 0's place
-  {
-    const int kbl = tid >> 4, q = tid & 15;
-    for (int kb0 = 0; kb0 < nkb; kb0 += 16) {
+  // 1. activation fragment of the token, chunk 0's place, by waves 1-3 (four
+  // k-blocks per wave and pass) while wave 0 routes
+  if (wave > 0) {
+    const int kbl = lane >> 4, q = lane & 15;
+    uint4 (&fw)[4][16] = fr[wave - 1];
+    for (int kb0 = 4 * (wave - 1); kb0 < nkb; kb0 += 12) {
       const int kb = kb0 + kbl;
       const bool on = kb < nkb;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(ONE_NT) void k_one(FfnShape s, PlanPtrs pp, const u
         X += xf;
         V += xf * sc;
         const int fp = frag_pos(cc);
-        reinterpret_cast<uint16_t*>(fr[kbl])[((fp >> 3) * 4 + (col >> 5)) * 8 + (fp & 7)] =
+        reinterpret_cast<uint16_t*>(fw[kbl])[((fp >> 3) * 4 + (col >> 5)) * 8 + (fp & 7)] =
             (uint16_t)f32_to_bf16(xf * sc);
       }
       for (int msk = 1; msk < tpg; msk <<= 1) {
@@ -249,13 +252,17 @@ __global__ __launch_bounds__(ONE_NT) void k_one(FfnShape s, PlanPtrs pp, const u
         V += __shfl_xor(V, msk, WAVE);
       }
       if (on && (q & (tpg - 1)) == 0) xvg[(size_t)(kb * (128 / s.g) + q / tpg) * 16] = make_float2(X, V);
-      __syncthreads();
+      // the wave's own LDS writes, then its reads of them (wave-level order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (on) {
         const int i = q >> 2, jg = q & 3;
-        reinterpret_cast<uint4*>(xg)[(size_t)kb * 256 + i * 64 + act_pos(0, 0, jg)] =
-            fr[kbl][q];
+        reinterpret_cast<uint4*>(xg)[(size_t)kb * 256 + i * 64 + act_pos(0, 0, jg)] = fw[kbl][q];
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 
