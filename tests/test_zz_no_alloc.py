@@ -49,17 +49,20 @@ def _both(w, dev, T, accumulate=False):
 def test_static_layer_equals_layer_qwen_two_calls():
     w, dev = _dev(2)
     assert bd.lib().moe_layer_static_scratch_bytes() == 64 << 20
-    note("layer_static cfg2 T=32 then T=5")
+    note("layer_static cfg2 T=32 then T=5, T=1")
     _both(w, dev, 32)
     _both(w, dev, 5, accumulate=True)
+    _both(w, dev, 1)                   # the one-token plan kernel on the static array
+    _both(w, dev, 1, accumulate=True)
     _both(w, dev, 32)
 
 
 def test_static_layer_equals_layer_deepseek_shared():
     w, dev = _dev(3)
-    note("layer_static cfg3 T=16 then T=3")
+    note("layer_static cfg3 T=16 then T=3, T=1")
     _both(w, dev, 16)
     _both(w, dev, 3)
+    _both(w, dev, 1)
 
 
 def test_static_layer_rejects_batches_beyond_the_array():
