@@ -122,19 +122,49 @@ __device__ void plan_chunks(const FfnShape& s, const PlanPtrs& pp, const int* of
     }
     int total;
     const int cbase = block_exclusive_scan(nch, wsum, &total);
-    if (e < E) {
-      for (int c = 0; c < nch; ++c) {
-        const int s0 = off[e * B] + s.cs * c;
-        const int mm = min(s.cs, m - s.cs * c);
+    if (total <= E) {
+      // at most as many chunks as experts (decode): one thread per expert
+      if (e < E) {
+        for (int c = 0; c < nch; ++c) {
+          const int s0 = off[e * B] + s.cs * c;
+          const int mm = min(s.cs, m - s.cs * c);
+          int mask = 0, cnt = 0;
+          for (int L = 0; L < B; ++L) {
+            const int lo = off[e * B + L], hi = off[e * B + L + 1];
+            if (hi > lo && hi > s0 && lo < s0 + mm) mask |= 1 << (B - L - 1);  // bit (b-1) for width b
+            // pairs of the chunk with width >= B - L
+            cnt |= min(max(hi - s0, 0), mm) << (8 * (B - L - 1));
+          }
+          pp.chunks[cbase + c] = make_int4(e, s0, mm, mask);
+          pp.chunk_cnt[cbase + c] = cnt;
+        }
+      }
+    } else {
+      // more chunks (large batches): the first chunk of every expert, then
+      // the chunks spread over the threads, so that a heavily loaded expert's
+      // chunks are not one thread's serial loop (the same records)
+      __shared__ int scb[257];
+      if (e < E) scb[e] = cbase;
+      __syncthreads();
+      for (int c = tid; c < total; c += PM_NT) {
+        // the chunk's expert: the largest e with scb[e] <= c
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (scb[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const int ce = lo, cc = c - scb[ce];
+        const int me = off[(ce + 1) * B] - off[ce * B];
+        const int s0 = off[ce * B] + s.cs * cc;
+        const int mm = min(s.cs, me - s.cs * cc);
         int mask = 0, cnt = 0;
         for (int L = 0; L < B; ++L) {
-          const int lo = off[e * B + L], hi = off[e * B + L + 1];
-          if (hi > lo && hi > s0 && lo < s0 + mm) mask |= 1 << (B - L - 1);  // bit (b-1) for width b
-          // pairs of the chunk with width >= B - L
-          cnt |= min(max(hi - s0, 0), mm) << (8 * (B - L - 1));
+          const int lo2 = off[ce * B + L], hi2 = off[ce * B + L + 1];
+          if (hi2 > lo2 && hi2 > s0 && lo2 < s0 + mm) mask |= 1 << (B - L - 1);
+          cnt |= min(max(hi2 - s0, 0), mm) << (8 * (B - L - 1));
         }
-        pp.chunks[cbase + c] = make_int4(e, s0, mm, mask);
-        pp.chunk_cnt[cbase + c] = cnt;
+        pp.chunks[c] = make_int4(ce, s0, mm, mask);
+        pp.chunk_cnt[c] = cnt;
       }
     }
     if (tid == 0) pp.meta[0] = total;
