@@ -1172,6 +1172,10 @@ __global__ __launch_bounds__(64 * KS_WAVES) __attribute__((amdgpu_waves_per_eu(f
 // computed.
 
 constexpr int WIDE_THREADS = 256;
+// LDS dwords per ring stage of the weights: per wave, two tiles' plane words
+// (64 per plane, up to four planes), then the tiles' scales and zeros of the
+// k-block's quant group (16 rows each)
+constexpr int WIDE_PL_STAGE = 4 * (2 * 256 + 64);
 
 template <int MODE, int QPK, int MASK>
 __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, const int* bprefix, int c, int e,
@@ -1242,12 +1246,12 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   typedef __attribute__((address_space(3))) void* lds_ptr;
   const __amdgpu_buffer_rsrc_t rpl =
       make_rsrc(M.planes + (size_t)pfirst * (plane_bytes / 4), (uint32_t)B * plane_bytes);
-  auto copy_planes = [&](int kb, int st) {
+  auto copy_planes = [&](int kb, uint32_t* pst) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int p = 0; p < BM; ++p)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rpl, (lds_ptr)(plds + ((st * 4 + wave) * 2 + t) * 256 + p * 64), 4,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rpl, (lds_ptr)(pst + (wave * 2 + t) * 256 + p * 64), 4,
                                                  lane * 4, (t ? t1off : t0off) + kb * 256 + p * plane_bytes, 0, 0);
   };
   struct Wts {
@@ -1267,14 +1271,14 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   // (lanes past the 16 QPK float2 copy what follows them, never read)
   const __amdgpu_buffer_rsrc_t rxs =
       make_rsrc(a.asum + (size_t)(c * NB + wave) * a.asum_stride, (uint32_t)a.asum_stride * 8);
-  auto copy_xs = [&](int kb, int buf) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr)(xsl + (buf * NB + wave) * 32), 4, lane * 4, kb * QPK * 128, 0, 0);
+  auto copy_xs = [&](int kb, float2* xst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr)(xst + wave * 32), 4, lane * 4, kb * QPK * 128, 0, 0);
   };
   // activation fragments of k-block kb for the four token blocks -> LDS
   // buffer: wave w copies token block w, 4 x 1 KiB
   const __amdgpu_buffer_rsrc_t ract = make_rsrc(actc + (size_t)wave * a.act_stride, (uint32_t)a.act_stride * 2);
-  auto copy_act = [&](int kb, int buf) {
-    uint4* dst = lds + (size_t)(buf * NB + wave) * 256;
+  auto copy_act = [&](int kb, uint4* ast) {
+    uint4* dst = ast + (size_t)wave * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ract, (lds_ptr)(dst + i * 64), 16, lane * 16, kb * 4096 + i * 1024, 0, 0);
@@ -1292,7 +1296,50 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   const uint32_t hmask0 = (QPK == 2 && (jg >> 1) != 0) ? 0u : 0xFFFFFFFFu;
   const uint32_t hmask1 = (QPK == 2 && (jg >> 1) != 1) ? 0u : 0xFFFFFFFFu;
 
-  auto compute = [&](const Wts& o, int kb, int buf) {
+  // One quant group per k-block: the tiles' scales and zeros also travel
+  // through LDS, one copy per k-block (lanes 0..31 the 16 scales and 16 zeros
+  // of the first tile, lanes 32..63 those of the second), so no stage of the
+  // ring holds registers that a later wait would have to cover.
+  constexpr bool SZ_LDS = (QPK == 1);
+  const uint32_t vo_w = (lane < 32 ? s0off : s1off) + (uint32_t)(lane & 31) * 4;
+  auto copy_w = [&](int kb, uint32_t* pst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(pst + 4 * 2 * 256 + wave * 64), 4, vo_w, kb * 128, 0, 0);
+  };
+  // A k-block's small operands (scales and zeros, group sums, plane words),
+  // read from LDS right after the step's barrier, before the next stage's
+  // copies are issued, so that no read of them waits for those copies.
+  struct Small {
+    float s[2], z[2];
+    float2 xv[NB];
+    uint32_t pw[2][4];
+  };
+  auto load_small = [&](const float2* xst, const uint32_t* pst, Small& sm) {
+    if (SZ_LDS) {
+      const float* sc = reinterpret_cast<const float*>(pst + 4 * 2 * 256) + wave * 64;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sm.s[t] = sc[(t * 2 + 0) * 16 + r16];
+        sm.z[t] = sc[(t * 2 + 1) * 16 + r16];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sm.xv[b] = xst[b * 32 + (jg % QPK) * 16 + r16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t* pw = pst + (wave * 2 + t) * 256 + lane;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) sm.pw[t][p] = p < BM ? pw[p * 64] : 0u;
+    }
+  };
+  auto compute = [&](const Wts& o_reg, int kb, const uint4* ast, const Small& sm) {
+    Wts o = o_reg;
+    if (SZ_LDS) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        o.s[t][0] = sm.s[t];
+        o.z[t][0] = sm.z[t];
+      }
+    }
     // the blocks' widths, re-read per k-block so that the branch conditions
     // derived from them are not kept live (as lane masks) across the stream
     int presk = pres;
@@ -1301,7 +1348,7 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     const bool sel = (jg / QPK) == (kb % SPB);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float2 xv = xsl[(buf * NB + b) * 32 + (jg % QPK) * 16 + r16];
+      const float2 xv = sm.xv[b];
       const float X = sel ? xv.x : 0.f, V = sel ? xv.y : 0.f;
       cAk[b] += ctA[b] * X - 128.0f * FA[b] * V;
       cAx[b] += X;
@@ -1322,11 +1369,10 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     u32x4_t W[TP][4][4];
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
-      const uint32_t* pw = plds + ((buf * 4 + wave) * 2 + t0 + t) * 256 + lane;
-      const uint32_t n3 = pw[0];
-      const uint32_t n2 = BM > 1 ? pw[64] : 0u;
-      const uint32_t n1 = BM > 2 ? pw[128] : 0u;
-      const uint32_t n0 = BM > 3 ? pw[192] : 0u;
+      const uint32_t n3 = sm.pw[t0 + t][0];
+      const uint32_t n2 = sm.pw[t0 + t][1];
+      const uint32_t n1 = sm.pw[t0 + t][2];
+      const uint32_t n0 = sm.pw[t0 + t][3];
       unpack_nib(n3, n2, n1, n0, ubias, nk, W[t][BM - 1]);
       if (MASK & ((1 << (BM - 1)) - 1)) {
         // keep each widest word one AND-OR (re-associating it with the
@@ -1352,13 +1398,13 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
     // block's (double-buffered by block parity) while this one runs.
     u32x4_t av[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[0][i] = as_u32x4(lds[(size_t)(buf * NB) * 256 + lane + i * 64]);
+    for (int i = 0; i < 4; ++i) av[0][i] = as_u32x4(ast[lane + i * 64]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int cb = b & 1;
       if (b + 1 < NB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[cb ^ 1][i] = as_u32x4(lds[(size_t)(buf * NB + b + 1) * 256 + lane + i * 64]);
+        for (int i = 0; i < 4; ++i) av[cb ^ 1][i] = as_u32x4(ast[(size_t)(b + 1) * 256 + lane + i * 64]);
       }
       const int pb = (presk >> (4 * b)) & 15;
 #pragma unroll
@@ -1432,34 +1478,67 @@ __device__ __forceinline__ void run_wide(const FfnArgs& a, const MatrixDev& M, c
   };
 
   // Three-stage ring: k-block kb+2's copies and weight loads are issued
-  // once every wave has passed k-block kb's barrier (so its LDS buffer,
-  // last read at kb-1, is free) and run while kb and kb+1 are computed.
+  // once every wave has passed k-block kb's barrier (so its LDS buffers,
+  // last read at kb-1, are free) and run while kb and kb+1 are computed.
   // Every stage issues the same NS vector loads and they retire in issue
   // order, so waiting for all but the newest NS leaves exactly stage kb+1 in
-  // flight.
-  constexpr int NS = 4 + 1 + 2 * BM + 4 * QPK;  // activation and group-sum copies, plane copies, scales and zeros
-  Wts wr[3];
-  auto issue = [&](int kb, int st) {
-    copy_act(kb, st);
-    copy_xs(kb, st);
-    copy_planes(kb, st);
-    load_w(kb, wr[st]);
+  // flight.  A step takes the buffers of the stage it computes and of the
+  // stage it fills as distinct restrict pointers: the LDS reads of one are
+  // then known not to alias the copies into the other, and wait only for
+  // their own stage (with one buffer array the compiler made every read wait
+  // for the copies just issued).
+  constexpr int NS = 4 + 1 + 2 * BM + (SZ_LDS ? 1 : 4 * QPK);  // activation and group-sum copies, plane copies, scales and zeros
+  Wts wr[3] = {};
+  auto stage_a = [&](int st) { return lds + (size_t)st * NB * 256; };
+  auto stage_x = [&](int st) { return xsl + st * NB * 32; };
+  auto stage_p = [&](int st) { return plds + st * WIDE_PL_STAGE; };
+  auto step = [&](int kb, const Wts& wcur, Wts& wnxt, const uint4* __restrict__ acur, const float2* __restrict__ xcur,
+                  const uint32_t* __restrict__ pcur, uint4* __restrict__ anxt, float2* __restrict__ xnxt,
+                  uint32_t* __restrict__ pnxt) {
+    if (kb + 1 < NKB)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // A plain barrier, without __syncthreads' release fence: that fence waits
+    // for every copy still in flight (stage kb+1 too).  Each wave has waited
+    // for its own copies of stage kb above, and has consumed its reads of
+    // stage kb-1 (the one refilled next) before arriving; the empty asm
+    // statements keep the compiler's memory accesses on their side.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Small sm;
+    load_small(xcur, pcur, sm);
+    if (kb + 2 < NKB) {
+      copy_act(kb + 2, anxt);
+      copy_xs(kb + 2, xnxt);
+      copy_planes(kb + 2, pnxt);
+      if (SZ_LDS) copy_w(kb + 2, pnxt); else load_w(kb + 2, wnxt);
+    }
+    compute(wcur, kb, acur, sm);
   };
-  issue(0, 0);
-  if (NKB > 1) issue(1, 1);
+  // the first two stages' copies (restrict pointers too, so that the reads
+  // of the first steps know which copies they wait for)
+  auto prime = [&](int kb, uint4* __restrict__ an, float2* __restrict__ xn, uint32_t* __restrict__ pn, Wts& wn) {
+    copy_act(kb, an);
+    copy_xs(kb, xn);
+    copy_planes(kb, pn);
+    if (SZ_LDS) copy_w(kb, pn); else load_w(kb, wn);
+  };
+  prime(0, stage_a(0), stage_x(0), stage_p(0), wr[0]);
+  if (NKB > 1) prime(1, stage_a(1), stage_x(1), stage_p(1), wr[1]);
+  // both first stages in before the loop: no copy of the prologue is left in
+  // flight at the loop's head, where the compiler would otherwise make the
+  // loop's reads wait for every copy on every pass
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // one call site of the step, unrolled three ways, so every pass carries the
+  // same alias information
   for (int kb0 = 0; kb0 < NKB; kb0 += 3) {
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const int kb = kb0 + q;
-      if (kb < NKB) {
-        if (kb + 1 < NKB)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NS));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        if (kb + 2 < NKB) issue(kb + 2, (q + 2) % 3);
-        compute(wr[q], kb, q);
-      }
+      const int nq = (q + 2) % 3;
+      if (kb0 + q < NKB)
+        step(kb0 + q, wr[q], wr[nq], stage_a(q), stage_x(q), stage_p(q), stage_a(nq), stage_x(nq), stage_p(nq));
     }
   }
 
@@ -1515,7 +1594,7 @@ template <int MODE, int QPK>
 __global__ __launch_bounds__(WIDE_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_wide(FfnArgs a) {
   __shared__ uint4 lds[3 * 4 * 256];   // three k-blocks x four token blocks x 4 KiB
   __shared__ float2 xsl[3 * 4 * 32];   // their group sums
-  __shared__ uint32_t plds[3 * 4 * 2 * 4 * 64];  // per k-block, wave, tile and plane: 64 plane words
+  __shared__ uint32_t plds[3 * WIDE_PL_STAGE];  // per k-block and wave: 64 words per tile and plane, then 64 scales and zeros
   // Workgroup b runs on XCD b mod 8 and takes item (b / 8) of that XCD's
   // contiguous eighth of the call's items: the items of one chunk (which
   // share its activations) and the chunks of one expert (which share its
