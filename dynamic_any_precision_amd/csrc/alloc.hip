@@ -115,18 +115,62 @@ __global__ __launch_bounds__(NT) void k_alloc_radix(const float* __restrict__ ga
     keys[i] = idx < P ? order_key(gate[idx]) : 0u;
   }
   const int in_regs = NT * AL_VPT;
-  uint32_t prefix = 0u;
+  // The keys' common leading bits (from their minimum and maximum) are the
+  // answer's leading bits already; the first digit is the 8 bits below them,
+  // so its histogram spreads over many bins (gates share their top key bits,
+  // and a first digit of the top 8 bits put them all on a few bins, where
+  // the atomics serialise).  Then 8-bit digits down to bit 0.
+  __shared__ uint32_t s_mm[2 * (NT / WAVE)];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < AL_VPT; ++i)
+    if (tid + i * NT < P) {
+      kmin = min(kmin, keys[i]);
+      kmax = max(kmax, keys[i]);
+    }
+  for (int idx = in_regs + tid; idx < P; idx += NT) {
+    const uint32_t k = order_key(gate[idx]);
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, WAVE));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, WAVE));
+  }
+  if (lane == 0) {
+    s_mm[2 * wave] = kmin;
+    s_mm[2 * wave + 1] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NT / WAVE; ++w) {
+    kmin = min(kmin, s_mm[2 * w]);
+    kmax = max(kmax, s_mm[2 * w + 1]);
+  }
+  // With n* < P the answer lies in [kmin, kmax] (at least one key is at or
+  // below it, none above kmax is needed), so it carries the keys' common
+  // leading bits; with n* >= P it is 0 and the descent starts from the top.
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = (diff && n_star < P) ? 31 - __clz((int)diff) : 31;  // highest bit where the keys differ
+  uint32_t prefix = hb >= 31 ? 0u : (kmin & ~((2u << hb) - 1u));
   int above = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  int shift = hb >= 7 ? hb - 7 : 0;
+  int width = hb - shift + 1;
+  for (;;) {
     for (int j = tid; j < 256; j += NT) hist[j] = 0;
     __syncthreads();
-    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    const uint32_t top = (uint32_t)(shift + width);
+    const uint32_t hmask = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+    const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
     for (int i = 0; i < AL_VPT; ++i)
-      if (tid + i * NT < P && (keys[i] & hmask) == prefix) atomicAdd(&hist[(keys[i] >> shift) & 255u], 1);
+      if (tid + i * NT < P && (keys[i] & hmask) == prefix) atomicAdd(&hist[(keys[i] >> shift) & dmask], 1);
     for (int idx = in_regs + tid; idx < P; idx += NT) {
       const uint32_t k = order_key(gate[idx]);
-      if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1);
     }
     __syncthreads();
     if (wave == 0) {
@@ -158,6 +202,9 @@ __global__ __launch_bounds__(NT) void k_alloc_radix(const float* __restrict__ ga
     __syncthreads();
     prefix = s_prefix;
     above = s_above;
+    if (shift == 0) break;
+    width = shift < 8 ? shift : 8;
+    shift -= width;
   }
 #pragma unroll
   for (int i = 0; i < AL_VPT; ++i) {
